@@ -1,0 +1,188 @@
+/*
+ * qstate.h — C ABI of the quantized recurrent-state decode library (gfx950).
+ *
+ * One decode step of a linear-attention / state-space layer whose fixed-size
+ * recurrent state S[b][h][dv][dk] is stored in INT8 or packed INT4 between
+ * steps.  Each step dequantizes the stored state, applies the full-precision
+ * update, reads out o = S'q and writes the state back through the quantizer.
+ *
+ * Sources (web pages on the method):
+ *  - "Quantizing Recurrent Language Models Is Easier Than You Think" (LoReS
+ *    blog), Fig. 1 "Recurrent state: overwrite": the recurrence takes q, k, v
+ *    and the previous state and overwrites the whole state through a
+ *    quantizer after each update.
+ *  - same page, "LoReS: State Quantization": updates stay in full precision,
+ *    only the state kept between decode steps is quantized; value-axis (row)
+ *    scale groups (1/4), decay-based per-head bits (2/4), stochastic rounding
+ *    (3/4); symmetric absmax scale s = max|S_G| / r, r = 2^(b-1) - 1
+ *    (Prop. "per-channel readout error" and 4/4 animation details).
+ *  - same page, Prop. "decaying error": delta correction with unit-norm keys
+ *    and 0 < beta < 2, decay |alpha|_inf < 1; Prop. "repeated quantization",
+ *    animation: the scalar-decay form S_t = alpha S_{t-1} + a v_t k_t^T.
+ *  - "Preserving Updates in Low-Bit Recurrent State Quantization" abstract:
+ *    Gated DeltaNet, GLA, Mamba2 and RetNet as the recurrences in question,
+ *    with savings measured against FP32 states.
+ *
+ * Semantics (exact, shared with the CPU checker; every FP32 operation below
+ * is one IEEE-754 binary32 operation with round-to-nearest-even unless noted):
+ *
+ *  Per head (b,h) with bit width n (4 or 8), r = 2^(n-1) - 1, and per value
+ *  row i (0 <= i < dv), key column j (0 <= j < dk), group g = j / G:
+ *   1. decayed dequantized row
+ *        GDN, SCALAR: d_j = c_ij * (s_ig * alpha)
+ *        GLA:         d_j = (c_ij * s_ig) * alpha_j
+ *        (FP32 state: d_j = S_ij * alpha   or   S_ij * alpha_j)
+ *   2. write weight
+ *        GDN:    u = dot(d, k);  w = beta * (v_i - u)
+ *        GLA:    w = v_i
+ *        SCALAR: w = beta * v_i          (beta carries Mamba2's dt)
+ *   3. S'_ij = fma(w, k_j, d_j)
+ *      so GDN computes S' = alpha S (I - beta k k^T) + beta v k^T,
+ *      GLA S' = S diag(alpha) + v k^T, SCALAR S' = alpha S + dt v k^T.
+ *   4. o_i = dot(S'_i, q)       (from the full-precision S', before requant)
+ *   5. m = max_{j in g} |S'_ij|;  m == 0: s' = 0, inv = 0, codes 0;
+ *      else s' = m / r (correctly rounded), inv = the largest float with
+ *      inv * m <= r (r / m rounded toward zero), so |S' * inv| <= r.
+ *   6. RTN: code = round-half-even(S'_ij * inv)   (exact product)
+ *      SR:  code = floor(fma(S'_ij, inv, u_ij)), u_ij = R16_ij * 2^-16
+ *      No clamp is ever active: both stay within [-r, r].
+ *   dot(x, y): 16-element chunks, each accumulated p = fma(x_j, y_j, p) from
+ *   p = 0 in ascending j, then a pairwise tree over the chunk partials
+ *   (((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) for dk = 128).
+ *
+ *  Stochastic-rounding bits R16_ij (counter-based, a pure function of
+ *  (seed, layer, step, b, h, element)):
+ *   key  = F(F(F(F(F(0 ^ seed + g) ^ layer + g) ^ step + g) ^ b + g) ^ h + g),
+ *          i.e. x = F((x XOR v) + g) for v = seed, layer, step, b, h from
+ *          x = 0, where F is the SplitMix64 output function and
+ *          g = 0x9E3779B97F4A7C15;  K = (uint32)(key >> 32) ^ (uint32)key.
+ *   e = i*dk + j (element index within the head), block q = e / 16,
+ *   pair p = (e % 16) / 2.
+ *   z_q = max(fmix32(K ^ q), 1)          (MurmurHash3 32-bit finalizer)
+ *   W   = xorshift32^p (z_q)             (Marsaglia 2003, shifts 13,17,5)
+ *   R16 = W & 0xFFFF for even e, W >> 16 for odd e.
+ *  Each quantization event (a step, or an FP32 import) uses the handle's
+ *  current step counter and then increments it.
+ *
+ * Layout (all device buffers are caller-owned, 16-byte aligned, contiguous):
+ *   q, k            float [B][H][dk]
+ *   v, o            float [B][H][dv]
+ *   alpha           float [B][H]      (GDN, SCALAR)  or  [B][H][dk] (GLA)
+ *   beta            float [B][H]      (GDN: beta, SCALAR: dt; GLA: unused)
+ *   codes           heads in (b, h) order; head (b,h) starts at byte
+ *                   b*P + sum_{h'<h} dv*dk*n_{h'}/8, P = sum_h dv*dk*n_h/8.
+ *                   Row-major [dv][dk] inside a head.  INT8: int8 two's
+ *                   complement.  INT4: two's-complement nibbles, byte
+ *                   (i*dk + j)/2 holds even j in bits 0..3, odd j in 4..7.
+ *   scales          float [B][H][dv][dk/G]
+ *   FP32 state      float [B][H][dv][dk]  (fp32_state = 1)
+ *
+ * Ownership: the library never allocates or frees device memory; a handle
+ * owns only host memory.  The state is updated in place.  o must not alias
+ * any input.  Calls are asynchronous on the given HIP stream (NULL = the
+ * default stream); device faults surface at the caller's next
+ * synchronisation.  A handle must not be used from two threads at once.
+ *
+ * Errors: every call returns QSTATE_OK (0) or a negative QSTATE_E_* code.
+ * Argument checks are synchronous and happen before any launch; a failed
+ * check leaves the handle and the buffers untouched.
+ */
+#ifndef QSTATE_H
+#define QSTATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QSTATE_OK = 0,
+  QSTATE_E_INVALID = -1,     /* null/misaligned pointer, bad size or enum  */
+  QSTATE_E_UNSUPPORTED = -2, /* valid but not built: shape, group, heads   */
+  QSTATE_E_LAUNCH = -3,      /* the HIP runtime refused a launch           */
+  QSTATE_E_NOMEM = -4        /* host allocation of the handle failed       */
+};
+
+typedef enum {
+  QSTATE_GDN = 0,    /* S' = a S (I - b k k^T) + b v k^T   (Gated DeltaNet) */
+  QSTATE_GLA = 1,    /* S' = S diag(alpha[dk]) + v k^T     (beta unused)    */
+  QSTATE_SCALAR = 2  /* S' = a S + b v k^T   (Mamba2 with b = dt; RetNet)   */
+} qstate_mixer;
+
+typedef enum { QSTATE_RTN = 0, QSTATE_SR = 1 } qstate_rounding;
+
+typedef struct {
+  int32_t batch;            /* B >= 1                                         */
+  int32_t heads;            /* H, 1..256                                      */
+  int32_t dk;               /* key dim (columns): 64, 128 or 256              */
+  int32_t dv;               /* value dim (rows): 1..4096                      */
+  int32_t group;            /* G: 16, 32, 64 or 128, divides dk               */
+  int32_t mixer;            /* qstate_mixer                                   */
+  int32_t rounding;         /* qstate_rounding                                */
+  int32_t fp32_state;       /* 1: unquantized FP32 state (baseline); the
+                               group, rounding and head_bits are ignored      */
+  const uint8_t* head_bits; /* host [heads], each 4 or 8; copied at create;
+                               NULL = all 8                                   */
+  uint64_t seed;            /* stochastic-rounding key                        */
+  uint32_t layer;           /* stochastic-rounding key                        */
+} qstate_config;
+
+typedef struct qstate qstate; /* opaque; host-side metadata only */
+
+/* Sizes in bytes of the caller-owned state buffers for cfg.  For an FP32
+ * state, *codes_bytes is the FP32 state size and *scales_bytes is 0. */
+int qstate_state_bytes(const qstate_config* cfg, size_t* codes_bytes,
+                       size_t* scales_bytes);
+
+/* Validate cfg, record the two state buffers (device pointers; scales_dev
+ * ignored for an FP32 state) and return a handle with step counter 0.
+ * Host only: no device work, no device allocation. */
+int qstate_create(const qstate_config* cfg, void* codes_dev, void* scales_dev,
+                  qstate** out);
+
+/* Import: quantize the FP32 state S_dev [B][H][dv][dk] into the handle's
+ * codes and scales (steps 5-6 above, counter = current step), then step++.
+ * For an FP32 handle this is a device copy and the counter is unchanged. */
+int qstate_load_fp32(qstate* h, const float* S_dev, void* stream);
+
+/* The decode step (steps 1-6 above) for every head, in place; o may be NULL.
+ * alpha: [B][H] (GDN, SCALAR) or [B][H][dk] (GLA); beta: [B][H] (GDN,
+ * SCALAR), ignored for GLA.  Increments the step counter. */
+int qstate_step(qstate* h, const float* q, const float* k, const float* v,
+                const float* alpha, const float* beta, float* o, void* stream);
+
+/* Readout without update: o_i = dot(c_ij * s_ig, q) (FP32 state: dot(S, q)).
+ * The counter is unchanged. */
+int qstate_readout(qstate* h, const float* q, float* o, void* stream);
+
+/* Export the dequantized state S_ij = c_ij * s_ig into S_dev (FP32 state:
+ * a copy).  The counter is unchanged. */
+int qstate_store_fp32(qstate* h, float* S_dev, void* stream);
+
+/* Step counter (the stochastic-rounding counter used by the next event). */
+int qstate_get_step(const qstate* h, uint64_t* step);
+int qstate_set_step(qstate* h, uint64_t step);
+
+/* Free the handle (host memory only).  NULL is accepted. */
+int qstate_destroy(qstate* h);
+
+/* Static message for a status code. */
+const char* qstate_strerror(int status);
+
+/* Decay-based per-head bit allocation ("allocate more bits to the slowest-
+ * decaying heads", LoReS 2/4).  retention[h] is larger for slower decay
+ * (e.g. alpha_h, or exp(-softplus(A_h))).
+ *   mode 0: out[h] = hi if retention[h] > thr_or_frac else lo
+ *   mode 1: the round(thr_or_frac * heads) heads with the largest retention
+ *           get hi (ties: the lower head index first), the rest lo. */
+int qstate_bits_by_decay(const float* retention, int heads, int mode,
+                         float thr_or_frac, uint8_t lo_bits, uint8_t hi_bits,
+                         uint8_t* out_bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSTATE_H */

@@ -1,0 +1,408 @@
+// oracle.cpp — plain, slow, single-threaded CPU reference of the quantized
+// recurrent-state decode step.  TEST INFRASTRUCTURE ONLY (see oracle.h): the
+// product library never includes, links or calls it.
+//
+// Build: g++ -std=c++17 -O2 -ffp-contract=off -fPIC -shared (no fast-math).
+// Float arithmetic is IEEE binary32 with round-to-nearest-even; std::fma is
+// the correctly rounded fused multiply-add; products that must be exact are
+// formed in double, where the product of two floats is exact.
+
+#include "oracle.h"
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+namespace {
+
+const int kMixerGDN = 0, kMixerGLA = 1;
+const int kRoundSR = 1;
+
+int qmax(int bits) { return (1 << (bits - 1)) - 1; }  // r = 2^(b-1) - 1
+
+}  // namespace
+
+extern "C" {
+
+// ---------------------------------------------------------------------------
+// Counter-based random bits for stochastic rounding.
+// The pages ask only for conditionally unbiased rounding (LoReS 3/4,
+// "Rounding"); the bits are a pure function of (seed, layer, step, b, h,
+// element) so that any implementation draws the same ones.
+// ---------------------------------------------------------------------------
+
+// SplitMix64 output function (Steele, Lea & Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014; constants of Stafford's
+// "Mix13" variant as used by SplitMix64).
+uint64_t oracle_splitmix64_output(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// 32-bit finalizer of MurmurHash3 (Appleby, public domain).
+uint32_t oracle_fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Marsaglia, "Xorshift RNGs", J. Stat. Softw. 8(14), 2003: shifts 13, 17, 5.
+uint32_t oracle_xorshift32(uint32_t y) {
+  y ^= y << 13;
+  y ^= y >> 17;
+  y ^= y << 5;
+  return y;
+}
+
+// Per-(seed, layer, step, b, h) key: each field is absorbed through the
+// SplitMix64 output function, x = F((x ^ v) + golden), starting from x = 0.
+uint32_t oracle_head_key(uint64_t seed, uint32_t layer, uint64_t step,
+                         uint32_t b, uint32_t h) {
+  const uint64_t golden = 0x9E3779B97F4A7C15ull;
+  const uint64_t fields[5] = {seed, layer, step, b, h};
+  uint64_t x = 0;
+  for (uint64_t v : fields) x = oracle_splitmix64_output((x ^ v) + golden);
+  return (uint32_t)(x >> 32) ^ (uint32_t)x;
+}
+
+// The 16 random bits of element e of a head: blocks of 16 elements share one
+// hashed seed, and the 8 element pairs of a block walk a xorshift32 stream.
+uint32_t oracle_sr_bits(uint32_t key, uint64_t element) {
+  const uint32_t block = (uint32_t)(element / 16);
+  const int pair = (int)((element % 16) / 2);
+  uint32_t w = oracle_fmix32(key ^ block);
+  if (w == 0) w = 1;  // xorshift32 never leaves 0
+  for (int p = 0; p < pair; ++p) w = oracle_xorshift32(w);
+  return (element % 2 == 0) ? (w & 0xFFFFu) : (w >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Scalar pieces.
+// ---------------------------------------------------------------------------
+
+// Dot product in FP32: the pages fix no order, so one is written down.
+// Consecutive 16-element chunks are each accumulated with fused multiply-adds
+// from 0 in ascending index; the chunk partials are then summed pairwise,
+// adjacent pairs first, an odd last partial carried to the next level.
+float oracle_dot(const float* x, const float* y, int n) {
+  std::vector<float> part;
+  for (int c0 = 0; c0 < n; c0 += 16) {
+    float p = 0.0f;
+    for (int j = c0; j < std::min(n, c0 + 16); ++j) p = std::fma(x[j], y[j], p);
+    part.push_back(p);
+  }
+  if (part.empty()) return 0.0f;
+  while (part.size() > 1) {
+    std::vector<float> next;
+    for (size_t i = 0; i + 1 < part.size(); i += 2) next.push_back(part[i] + part[i + 1]);
+    if (part.size() % 2 == 1) next.push_back(part.back());
+    part.swap(next);
+  }
+  return part[0];
+}
+
+// Symmetric absmax scale of a group (LoReS 4/4: s = |S_G|_inf / r, with
+// r = 2^(b-1) - 1 from Prop. "per-channel readout error").  The scaled value
+// is formed with inv, the largest float whose product with m does not exceed
+// r, so that no scaled value leaves [-r, r].  An all-zero group gets s = 0.
+void oracle_group_scale(float m, int r, float* s, float* inv) {
+  if (m == 0.0f) {
+    *s = 0.0f;
+    *inv = 0.0f;
+    return;
+  }
+  *s = m / (float)r;
+  float v = (float)((double)r / (double)m);
+  while ((double)v * (double)m > (double)r) v = std::nextafter(v, 0.0f);
+  *inv = v;
+}
+
+// Round-to-nearest (LoReS 3/4 "RTN"): nearest integer to the exact product,
+// ties to even.  The double product of two floats is exact.
+int oracle_round_rtn(float x, float inv) {
+  return (int)std::rint((double)x * (double)inv);
+}
+
+// Stochastic rounding (LoReS 3/4, conditionally unbiased): floor(x*inv + u)
+// with u = r16 / 2^16, the sum formed by one fused multiply-add.
+int oracle_round_sr(float x, float inv, uint32_t r16) {
+  const float u = (float)(r16 & 0xFFFFu) * (1.0f / 65536.0f);
+  return (int)std::floor(std::fma(x, inv, u));
+}
+
+// ---------------------------------------------------------------------------
+// Layout: codes of head (b, h) start at b*P + sum_{h'<h} dv*dk*bits_h'/8.
+// INT8 codes are int8; INT4 codes are two's-complement nibbles, even element
+// in the low nibble.
+// ---------------------------------------------------------------------------
+
+static size_t head_bytes(const oracle_cfg* c, int bits) {
+  return (size_t)c->dv * (size_t)c->dk * (size_t)bits / 8;
+}
+
+size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* head_bits) {
+  size_t per_b = 0;
+  for (int h = 0; h < c->H; ++h) per_b += head_bytes(c, head_bits[h]);
+  return per_b * (size_t)c->B;
+}
+
+size_t oracle_head_offset(const oracle_cfg* c, const uint8_t* head_bits, int b,
+                          int h) {
+  size_t per_b = 0, before = 0;
+  for (int hh = 0; hh < c->H; ++hh) {
+    if (hh < h) before += head_bytes(c, head_bits[hh]);
+    per_b += head_bytes(c, head_bits[hh]);
+  }
+  return (size_t)b * per_b + before;
+}
+
+int oracle_get_code(const uint8_t* codes, int bits, int64_t e) {
+  if (bits == 8) return (int)(int8_t)codes[e];
+  const uint8_t byte = codes[e / 2];
+  const int nib = (e % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+void oracle_set_code(uint8_t* codes, int bits, int64_t e, int code) {
+  if (bits == 8) {
+    codes[e] = (uint8_t)(int8_t)code;
+    return;
+  }
+  const uint8_t nib = (uint8_t)(code & 0xF);
+  uint8_t& byte = codes[e / 2];
+  if (e % 2 == 0)
+    byte = (uint8_t)((byte & 0xF0) | nib);
+  else
+    byte = (uint8_t)((byte & 0x0F) | (nib << 4));
+}
+
+// ---------------------------------------------------------------------------
+// Requantization of one value row (LoReS: value-axis grouping, 1/4; the scale
+// is taken from the state being stored, 4/4 "noisy" scale).
+// ---------------------------------------------------------------------------
+
+static void quantize_row(const oracle_cfg* c, int bits, uint32_t key, int i,
+                         const float* row, uint8_t* codes, float* scales,
+                         double* xval) {
+  const int dk = c->dk, G = c->G, ng = dk / G, r = qmax(bits);
+  for (int g = 0; g < ng; ++g) {
+    float m = 0.0f;
+    for (int j = g * G; j < (g + 1) * G; ++j) m = std::max(m, std::fabs(row[j]));
+    float s, inv;
+    oracle_group_scale(m, r, &s, &inv);
+    scales[(size_t)i * ng + g] = s;
+    for (int j = g * G; j < (g + 1) * G; ++j) {
+      const int64_t e = (int64_t)i * dk + j;
+      int n;
+      if (c->rounding == kRoundSR) {
+        const uint32_t r16 = oracle_sr_bits(key, (uint64_t)e);
+        n = oracle_round_sr(row[j], inv, r16);
+        if (xval) {
+          const float u = (float)r16 * (1.0f / 65536.0f);
+          xval[e] = (double)std::fma(row[j], inv, u);
+        }
+      } else {
+        n = oracle_round_rtn(row[j], inv);
+        if (xval) xval[e] = (double)row[j] * (double)inv;
+      }
+      n = std::max(-r, std::min(r, n));
+      oracle_set_code(codes, bits, e, n);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One decode step of one head.  Fig. 1 "Recurrent state: overwrite": the
+// recurrence reads the stored state and overwrites all of it through the
+// quantizer; "LoReS: State Quantization": the update itself is full
+// precision.  Update forms: Gated DeltaNet S' = a S (I - b k k^T) + b v k^T
+// (Prop. "decaying error": unit keys, 0 < b < 2); GLA S' = S diag(alpha) +
+// v k^T; scalar decay S' = a S + dt v k^T (Prop. "repeated quantization",
+// animation details).  Readout o = S' q from the unquantized S'.
+// ---------------------------------------------------------------------------
+
+void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
+                      uint8_t* codes, float* scales, const float* q,
+                      const float* k, const float* v, const float* alpha,
+                      float beta, float* o, uint64_t step, float* pre,
+                      double* xval) {
+  const int dk = c->dk, dv = c->dv, G = c->G, ng = dk / G;
+  const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
+  std::vector<float> d(dk), sp(dk);
+  for (int i = 0; i < dv; ++i) {
+    // dequantize and decay
+    for (int j = 0; j < dk; ++j) {
+      const float code = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j);
+      const float s = scales[(size_t)i * ng + j / G];
+      if (c->mixer == kMixerGLA)
+        d[j] = (code * s) * alpha[j];
+      else
+        d[j] = code * (s * alpha[0]);
+    }
+    // write weight
+    float w;
+    if (c->mixer == kMixerGDN) {
+      const float u = oracle_dot(d.data(), k, dk);
+      w = beta * (v[i] - u);
+    } else if (c->mixer == kMixerGLA) {
+      w = v[i];
+    } else {
+      w = beta * v[i];
+    }
+    // rank-1 write
+    for (int j = 0; j < dk; ++j) sp[j] = std::fma(w, k[j], d[j]);
+    if (o) o[i] = oracle_dot(sp.data(), q, dk);
+    if (pre) std::memcpy(pre + (size_t)i * dk, sp.data(), sizeof(float) * dk);
+    quantize_row(c, bits, key, i, sp.data(), codes, scales, xval);
+  }
+}
+
+// The same step on an unquantized FP32 state (the "FP32 states" the pages
+// compare against).
+void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
+                           const float* k, const float* v, const float* alpha,
+                           float beta, float* o) {
+  const int dk = c->dk, dv = c->dv;
+  std::vector<float> d(dk);
+  for (int i = 0; i < dv; ++i) {
+    float* row = S + (size_t)i * dk;
+    for (int j = 0; j < dk; ++j)
+      d[j] = row[j] * (c->mixer == kMixerGLA ? alpha[j] : alpha[0]);
+    float w;
+    if (c->mixer == kMixerGDN) {
+      const float u = oracle_dot(d.data(), k, dk);
+      w = beta * (v[i] - u);
+    } else if (c->mixer == kMixerGLA) {
+      w = v[i];
+    } else {
+      w = beta * v[i];
+    }
+    for (int j = 0; j < dk; ++j) row[j] = std::fma(w, k[j], d[j]);
+    if (o) o[i] = oracle_dot(row, q, dk);
+  }
+}
+
+void oracle_head_quantize(const oracle_cfg* c, int b, int h, int bits,
+                          const float* S, uint8_t* codes, float* scales,
+                          uint64_t step, double* xval) {
+  const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
+  for (int i = 0; i < c->dv; ++i)
+    quantize_row(c, bits, key, i, S + (size_t)i * c->dk, codes, scales, xval);
+}
+
+void oracle_head_dequantize(const oracle_cfg* c, int bits, const uint8_t* codes,
+                            const float* scales, float* S) {
+  const int dk = c->dk, G = c->G, ng = dk / G;
+  for (int i = 0; i < c->dv; ++i)
+    for (int j = 0; j < dk; ++j)
+      S[(size_t)i * dk + j] = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j) *
+                              scales[(size_t)i * ng + j / G];
+}
+
+void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
+                         const float* scales, const float* q, float* o) {
+  std::vector<float> S((size_t)c->dv * c->dk);
+  oracle_head_dequantize(c, bits, codes, scales, S.data());
+  for (int i = 0; i < c->dv; ++i) o[i] = oracle_dot(S.data() + (size_t)i * c->dk, q, c->dk);
+}
+
+// ---------------------------------------------------------------------------
+// Whole batch, in the library's array layout.
+// ---------------------------------------------------------------------------
+
+void oracle_step(const oracle_cfg* c, const uint8_t* head_bits, uint8_t* codes,
+                 float* scales, const float* q, const float* k, const float* v,
+                 const float* alpha, const float* beta, float* o, uint64_t step) {
+  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  const int na = (c->mixer == kMixerGLA) ? dk : 1;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t bh = (size_t)b * c->H + h;
+      oracle_head_step(c, b, h, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
+                       scales + bh * dv * ng, q + bh * dk, k + bh * dk, v + bh * dv,
+                       alpha + bh * na, (c->mixer == kMixerGLA) ? 0.0f : beta[bh],
+                       o ? o + bh * dv : nullptr, step, nullptr, nullptr);
+    }
+}
+
+void oracle_step_fp32(const oracle_cfg* c, float* S, const float* q, const float* k,
+                      const float* v, const float* alpha, const float* beta, float* o) {
+  const int dk = c->dk, dv = c->dv;
+  const int na = (c->mixer == kMixerGLA) ? dk : 1;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t bh = (size_t)b * c->H + h;
+      oracle_head_step_fp32(c, S + bh * dv * dk, q + bh * dk, k + bh * dk, v + bh * dv,
+                            alpha + bh * na, (c->mixer == kMixerGLA) ? 0.0f : beta[bh],
+                            o ? o + bh * dv : nullptr);
+    }
+}
+
+void oracle_quantize(const oracle_cfg* c, const uint8_t* head_bits, const float* S,
+                     uint8_t* codes, float* scales, uint64_t step) {
+  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t bh = (size_t)b * c->H + h;
+      oracle_head_quantize(c, b, h, head_bits[h], S + bh * dv * dk,
+                           codes + oracle_head_offset(c, head_bits, b, h),
+                           scales + bh * dv * ng, step, nullptr);
+    }
+}
+
+void oracle_dequantize(const oracle_cfg* c, const uint8_t* head_bits,
+                       const uint8_t* codes, const float* scales, float* S) {
+  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t bh = (size_t)b * c->H + h;
+      oracle_head_dequantize(c, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
+                             scales + bh * dv * ng, S + bh * dv * dk);
+    }
+}
+
+void oracle_readout(const oracle_cfg* c, const uint8_t* head_bits, const uint8_t* codes,
+                    const float* scales, const float* q, float* o) {
+  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t bh = (size_t)b * c->H + h;
+      oracle_head_readout(c, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
+                          scales + bh * dv * ng, q + bh * dk, o + bh * dv);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decay-based mixed precision (LoReS 2/4: more bits for the slowest-decaying
+// heads).  retention is larger for slower decay.
+//   mode 0: hi bits where retention > threshold;
+//   mode 1: hi bits for the round(frac * heads) heads of largest retention,
+//           ties resolved toward the lower head index.
+// ---------------------------------------------------------------------------
+
+int oracle_bits_by_decay(const float* retention, int heads, int mode,
+                         float thr_or_frac, uint8_t lo, uint8_t hi, uint8_t* out) {
+  if (heads <= 0) return -1;
+  if (mode == 0) {
+    for (int h = 0; h < heads; ++h) out[h] = retention[h] > thr_or_frac ? hi : lo;
+    return 0;
+  }
+  if (mode != 1 || !(thr_or_frac >= 0.0f && thr_or_frac <= 1.0f)) return -1;
+  const int n_hi = (int)std::floor((double)thr_or_frac * heads + 0.5);
+  std::vector<int> order(heads);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return retention[a] > retention[b]; });
+  for (int h = 0; h < heads; ++h) out[h] = lo;
+  for (int n = 0; n < n_hi; ++n) out[order[n]] = hi;
+  return 0;
+}
+
+}  // extern "C"

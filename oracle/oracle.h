@@ -1,0 +1,110 @@
+/*
+ * oracle.h — plain single-threaded CPU reference of the quantized
+ * recurrent-state decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant
+ * generator with the HIP library; the two implement the same written
+ * semantics independently.
+ *
+ * Every function follows the pages on the method ("Quantizing Recurrent
+ * Language Models Is Easier Than You Think", LoReS blog, section "LoReS:
+ * State Quantization" and Fig. 1) plus the readings stated where the pages
+ * are silent; the citation sits on each definition in oracle.cpp.
+ *
+ * Parity pins: see tests/test_oracle_*.py.  Each function below is pinned by
+ * a closed form, a brute-force search, a published test vector, an exact
+ * mathematical property or a statistical property of the method.  The
+ * particular 16-element-chunk summation order of dot() is a reading (any
+ * fixed order is equally correct); its result is pinned only to the exact
+ * dot product within the FP32 error bound.
+ */
+#ifndef QSTATE_ORACLE_H
+#define QSTATE_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t B, H, dk, dv, G;
+  int32_t mixer;    /* 0 Gated DeltaNet, 1 GLA, 2 scalar decay (Mamba2) */
+  int32_t rounding; /* 0 round-to-nearest-even, 1 stochastic            */
+  uint64_t seed;
+  uint32_t layer;
+} oracle_cfg;
+
+/* ---- counter-based random bits ---- */
+uint64_t oracle_splitmix64_output(uint64_t z);
+uint32_t oracle_fmix32(uint32_t h);
+uint32_t oracle_xorshift32(uint32_t y);
+uint32_t oracle_head_key(uint64_t seed, uint32_t layer, uint64_t step,
+                         uint32_t b, uint32_t h);
+uint32_t oracle_sr_bits(uint32_t key, uint64_t element);
+
+/* ---- scalar pieces ---- */
+float oracle_dot(const float* x, const float* y, int n);
+void oracle_group_scale(float m, int r, float* s, float* inv);
+int oracle_round_rtn(float x, float inv);
+int oracle_round_sr(float x, float inv, uint32_t r16);
+
+/* ---- layout ---- */
+size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* head_bits);
+size_t oracle_head_offset(const oracle_cfg* c, const uint8_t* head_bits,
+                          int b, int h);
+int oracle_get_code(const uint8_t* head_codes, int bits, int64_t e);
+void oracle_set_code(uint8_t* head_codes, int bits, int64_t e, int code);
+
+/* ---- one head (b, h): buffers point at that head's data ---- */
+/* alpha: 1 value (GDN, scalar) or dk values (GLA); beta: GDN beta / dt.
+ * o, pre, xval may be NULL.  pre receives S' [dv][dk] before requantizing;
+ * xval receives the pre-rounding value per element (RTN: the exact product
+ * S'*inv; SR: fma(S', inv, u)). */
+void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
+                      uint8_t* codes, float* scales, const float* q,
+                      const float* k, const float* v, const float* alpha,
+                      float beta, float* o, uint64_t step, float* pre,
+                      double* xval);
+void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
+                           const float* k, const float* v, const float* alpha,
+                           float beta, float* o);
+void oracle_head_quantize(const oracle_cfg* c, int b, int h, int bits,
+                          const float* S, uint8_t* codes, float* scales,
+                          uint64_t step, double* xval);
+void oracle_head_dequantize(const oracle_cfg* c, int bits,
+                            const uint8_t* codes, const float* scales,
+                            float* S);
+void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
+                         const float* scales, const float* q, float* o);
+
+/* ---- every head of a [B][H] batch, arrays in the library's layout ---- */
+void oracle_step(const oracle_cfg* c, const uint8_t* head_bits,
+                 uint8_t* codes, float* scales, const float* q,
+                 const float* k, const float* v, const float* alpha,
+                 const float* beta, float* o, uint64_t step);
+void oracle_step_fp32(const oracle_cfg* c, float* S, const float* q,
+                      const float* k, const float* v, const float* alpha,
+                      const float* beta, float* o);
+void oracle_quantize(const oracle_cfg* c, const uint8_t* head_bits,
+                     const float* S, uint8_t* codes, float* scales,
+                     uint64_t step);
+void oracle_dequantize(const oracle_cfg* c, const uint8_t* head_bits,
+                       const uint8_t* codes, const float* scales, float* S);
+void oracle_readout(const oracle_cfg* c, const uint8_t* head_bits,
+                    const uint8_t* codes, const float* scales, const float* q,
+                    float* o);
+
+/* ---- decay-based bit allocation (LoReS 2/4) ---- */
+int oracle_bits_by_decay(const float* retention, int heads, int mode,
+                         float thr_or_frac, uint8_t lo, uint8_t hi,
+                         uint8_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
