@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized recurrent-state decode step on one MI355X.
+
+A step is one qstate_step over the whole batch (every head: dequantize,
+update, readout, requantize).  The headline workload is the Gated DeltaNet
+decode at B=256, H=32, dk=dv=128, INT4 state with INT8 for the slowest-
+decaying heads, group 32, stochastic rounding.
+
+Cold protocol (the reported value): steps rotate over `--states` independent
+state instances (one per layer, each with its own stochastic-rounding key) so
+that the per-step working set is far larger than the 256 MB Infinity Cache,
+as in a model whose layers each hold a state; step inputs come from a pool of
+pre-generated batches already resident in HBM.  The hot number (one state,
+cache-resident) is reported beside it.
+
+Prints one JSON line.  The CPU reference is timed on a bounded sample of
+heads for the cpu_baseline figure.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-state decode steps/s and HBM GB/s (% of peak) at B=256, INT8/INT4"
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(w, hb) -> int:
+    """Bytes one step must move: each head's codes and scales read and written
+    once, q, k, v, o, and the gates (alpha per head or per key channel, beta)."""
+    per_b = 0
+    for h in range(w.H):
+        state = w.dv * w.dk * int(hb[h]) // 8 + w.dv * (w.dk // w.G) * 4
+        io = 4 * (2 * w.dk + 2 * w.dv)
+        gates = 4 * w.dk if w.mixer == 1 else 8
+        per_b += 2 * state + io + gates
+    return per_b * w.B
+
+
+def fp32_bytes(w) -> int:
+    per_head = 2 * w.dv * w.dk * 4 + 4 * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mixer == 1 else 8)
+    return per_head * w.B * w.H
+
+
+def cpu_baseline(w, hb, seconds: float):
+    """The CPU reference, single-threaded, on a sample of heads; scaled to steps/s."""
+    import oracle
+    import workloads as W
+
+    rng = np.random.default_rng(0)
+    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0)
+    q, k, v, alpha, beta = W.step_inputs(w, 0)
+    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096), rng.integers(0, w.H, 4096))]
+    S0 = rng.standard_normal((w.dv, w.dk)).astype(np.float32)
+    states = {}
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        b, h = heads[n % len(heads)]
+        if (b, h) not in states:
+            states[(b, h)] = oracle.head_quantize(c, b, h, int(hb[h]), S0, 0)[:2]
+        codes, scales = states[(b, h)]
+        a = alpha[b, h] if w.mixer == W.GLA else np.float32([alpha[b, h]])
+        oracle.head_step(c, b, h, int(hb[h]), codes, scales, q[b, h], k[b, h], v[b, h], a,
+                         0.0 if beta is None else float(beta[b, h]), 1 + n)
+        n += 1
+    dt = time.perf_counter() - t0
+    heads_per_s = n / dt
+    return {
+        "value": heads_per_s / (w.B * w.H),
+        "unit": "steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} head-steps of the same workload ({w.dv}x{w.dk} heads, mixed bits, "
+                  f"{'SR' if w.rounding else 'RTN'}) in {dt:.1f} s on one host thread, "
+                  f"scaled by the {w.B * w.H} heads of one step",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--rounding", type=int, default=None, help="override: 0 RTN, 1 SR")
+    ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
+    ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip hot/fp32/copy figures")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from bit_recurrent_state_amd import qstate as Q
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    w = W.WORKLOADS[args.workload]
+    if args.rounding is not None:
+        w = w.scaled(rounding=args.rounding)
+    policy = {"alpha_gt_0.99": (0, 0.99), "rank_half": (1, 0.5)}.get(w.bits_policy)
+    hb = (Q.qstate_bits_by_decay(W.head_retention(w), *policy) if policy
+          else np.full(w.H, 8, np.uint8))
+    nbytes = algorithmic_bytes(w, hb)
+
+    cfg0 = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0, 0)
+    cb, sb = Q.qstate_state_bytes(cfg0)
+    n_states = args.states or max(2, int(np.ceil(1.0 * 2**30 / (cb + sb))))
+
+    # initial state: FP32 warm-up on the GPU from zero, then the import
+    fcfg = Q.Config(w.B, w.H, w.dk, w.dv, 16, w.mixer, 0, True, None, 0, 0)
+    f = Q.QState(fcfg)
+    f.load_fp32(torch.zeros(w.B * w.H * w.dv * w.dk, device="cuda"))
+
+    def dev(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    for t in range(w.warmup):
+        f.step(*map(dev, W.step_inputs(w, t)))
+    S = torch.empty(w.B * w.H * w.dv * w.dk, device="cuda")
+    f.store_fp32(S)
+    f.close()
+    states = []
+    for layer in range(n_states):
+        cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0,
+                       layer)
+        s = Q.QState(cfg)
+        s.load_fp32(S)
+        states.append(s)
+    del S
+    pool = [tuple(map(dev, W.step_inputs(w, w.warmup + i))) for i in range(args.pool)]
+    o = torch.empty(w.B * w.H * w.dv, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def timed(run_states, steps, warm):
+        for i in range(warm):
+            run_states[i % len(run_states)].step(*pool[i % len(pool)], o)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            run_states[i % len(run_states)].step(*pool[i % len(pool)], o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per step
+
+    ms = timed(states, args.steps, args.warmup)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": 1e3 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "group": w.G,
+            "state_bits": {str(b): int((hb == b).sum()) for b in sorted(set(hb.tolist()))},
+            "rounding": "SR" if w.rounding else "RTN", "state_instances": n_states,
+            "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,
+        },
+        "hbm_gbps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": nbytes},
+    }
+
+    if not args.no_extras:
+        ms_hot = timed(states[:1], args.steps, args.warmup)
+        result["hot_single_state"] = {"ms_per_step": ms_hot, "steps_per_s": 1e3 / ms_hot,
+                                      "effective_gbps": nbytes / (ms_hot * 1e-3) / 1e9}
+        for s in states:
+            s.close()
+        states.clear()
+        torch.cuda.empty_cache()
+        # FP32-state baseline kernel, same protocol
+        fb = fp32_bytes(w)
+        n_f = max(2, int(np.ceil(1.0 * 2**30 / (fb / 2))))
+        fstates = []
+        for layer in range(n_f):
+            fs = Q.QState(Q.Config(w.B, w.H, w.dk, w.dv, 16, w.mixer, 0, True, None, 0, layer))
+            fs.load_fp32(torch.zeros(w.B * w.H * w.dv * w.dk, device="cuda"))
+            fstates.append(fs)
+        ms_f = timed(fstates, max(200, args.steps // 4), 10)
+        result["fp32_state_baseline"] = {
+            "ms_per_step": ms_f, "steps_per_s": 1e3 / ms_f, "state_instances": n_f,
+            "gbps": fb / (ms_f * 1e-3) / 1e9, "speedup_of_quantized": ms_f / ms}
+        for fs in fstates:
+            fs.close()
+        fstates.clear()
+        torch.cuda.empty_cache()
+        # plain device copy (read + write) as the box's achievable ceiling
+        n = 1 << 29
+        a = torch.empty(n, dtype=torch.float32, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            bb.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        result["copy_ceiling_gbps"] = 2 * 4 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del a, bb
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, hb, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+// qstate_api.cpp — the C ABI declared in include/qstate.h: argument checks,
+// the host-side handle, per-head layout and kernel dispatch.  Host code only;
+// every byte of the step is computed by the kernels in qstate_kernels.hip.
+
+#include "qstate.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "qstate_launch.h"
+
+struct qstate {
+  qstate_config cfg;      // head_bits pointer replaced by bits[]
+  uint8_t bits[256];
+  uint32_t int8_mask[8];
+  void* state;            // codes or FP32 state (device)
+  float* scales;          // device, quantized only
+  uint64_t step;
+  uint64_t bytes_per_b;   // code bytes of one batch row
+};
+
+namespace {
+
+constexpr int kMaxHeads = 256;
+constexpr int kMaxDv = 4096;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_config(const qstate_config* c) {
+  if (!c) return QSTATE_E_INVALID;
+  if (c->batch < 1 || c->heads < 1 || c->dk < 1 || c->dv < 1) return QSTATE_E_INVALID;
+  if (c->mixer < QSTATE_GDN || c->mixer > QSTATE_SCALAR) return QSTATE_E_INVALID;
+  if (c->fp32_state != 0 && c->fp32_state != 1) return QSTATE_E_INVALID;
+  if (!c->fp32_state) {
+    if (c->rounding != QSTATE_RTN && c->rounding != QSTATE_SR) return QSTATE_E_INVALID;
+    if (c->group < 1 || c->dk % c->group != 0) return QSTATE_E_INVALID;
+    if (c->head_bits)
+      for (int h = 0; h < c->heads && h < kMaxHeads; ++h)
+        if (c->head_bits[h] != 4 && c->head_bits[h] != 8) return QSTATE_E_INVALID;
+  }
+  if (c->dk != 64 && c->dk != 128 && c->dk != 256) return QSTATE_E_UNSUPPORTED;
+  if (c->heads > kMaxHeads || c->dv > kMaxDv) return QSTATE_E_UNSUPPORTED;
+  if (!c->fp32_state && c->group != 16 && c->group != 32 && c->group != 64 && c->group != 128)
+    return QSTATE_E_UNSUPPORTED;
+  // every index the kernels form must stay inside 63-bit sizes and a 32-bit grid
+  const double elems = (double)c->batch * c->heads * c->dv * c->dk;
+  if (elems * 4.0 > 9.0e18 || (double)c->batch * c->heads > 2147483647.0) return QSTATE_E_UNSUPPORTED;
+  return QSTATE_OK;
+}
+
+void layout(const qstate_config* c, size_t* codes_bytes, size_t* scales_bytes, uint64_t* per_b) {
+  const size_t bh = (size_t)c->batch * c->heads;
+  if (c->fp32_state) {
+    *codes_bytes = bh * c->dv * c->dk * sizeof(float);
+    *scales_bytes = 0;
+    if (per_b) *per_b = 0;
+    return;
+  }
+  uint64_t pb = 0;
+  for (int h = 0; h < c->heads; ++h) {
+    const int bits = c->head_bits ? c->head_bits[h] : 8;
+    pb += (uint64_t)c->dv * c->dk * bits / 8;
+  }
+  *codes_bytes = (size_t)pb * c->batch;
+  *scales_bytes = bh * c->dv * (c->dk / c->group) * sizeof(float);
+  if (per_b) *per_b = pb;
+}
+
+qs::KParams base_params(const qstate* s) {
+  qs::KParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.state = s->state;
+  p.scales = s->scales;
+  p.B = s->cfg.batch;
+  p.H = s->cfg.heads;
+  p.dv = s->cfg.dv;
+  p.G = s->cfg.fp32_state ? 16 : s->cfg.group;
+  p.bytes_per_b = s->bytes_per_b;
+  p.head_bytes4 = (uint32_t)((uint64_t)s->cfg.dv * s->cfg.dk / 2);
+  std::memcpy(p.int8_mask, s->int8_mask, sizeof(p.int8_mask));
+  p.seed = s->cfg.seed;
+  p.layer = s->cfg.layer;
+  p.step = s->step;
+  return p;
+}
+
+int run(const qstate* s, qs::Op op, const qs::KParams& p, void* stream) {
+  const qstate_config& c = s->cfg;
+  const hipError_t e = qs::launch(op, c.mixer, c.rounding, c.fp32_state, c.dk, p,
+                                  reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QSTATE_OK : QSTATE_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qstate_state_bytes(const qstate_config* cfg, size_t* codes_bytes, size_t* scales_bytes) {
+  const int rc = check_config(cfg);
+  if (rc != QSTATE_OK) return rc;
+  if (!codes_bytes || !scales_bytes) return QSTATE_E_INVALID;
+  layout(cfg, codes_bytes, scales_bytes, nullptr);
+  return QSTATE_OK;
+}
+
+int qstate_create(const qstate_config* cfg, void* codes_dev, void* scales_dev, qstate** out) {
+  if (!out) return QSTATE_E_INVALID;
+  *out = nullptr;
+  const int rc = check_config(cfg);
+  if (rc != QSTATE_OK) return rc;
+  if (!codes_dev || !aligned(codes_dev, 16)) return QSTATE_E_INVALID;
+  if (!cfg->fp32_state && (!scales_dev || !aligned(scales_dev, 16))) return QSTATE_E_INVALID;
+  qstate* s = new (std::nothrow) qstate;
+  if (!s) return QSTATE_E_NOMEM;
+  std::memset(s, 0, sizeof(*s));
+  s->cfg = *cfg;
+  for (int h = 0; h < cfg->heads; ++h) {
+    s->bits[h] = cfg->fp32_state ? 32 : (cfg->head_bits ? cfg->head_bits[h] : 8);
+    if (s->bits[h] == 8) s->int8_mask[h >> 5] |= 1u << (h & 31);
+  }
+  s->cfg.head_bits = nullptr;
+  size_t cb = 0, sb = 0;
+  qstate_config tmp = *cfg;
+  layout(&tmp, &cb, &sb, &s->bytes_per_b);
+  s->state = codes_dev;
+  s->scales = cfg->fp32_state ? nullptr : static_cast<float*>(scales_dev);
+  s->step = 0;
+  *out = s;
+  return QSTATE_OK;
+}
+
+int qstate_load_fp32(qstate* s, const float* S_dev, void* stream) {
+  if (!s || !S_dev || !aligned(S_dev, 16)) return QSTATE_E_INVALID;
+  const qstate_config& c = s->cfg;
+  if (c.fp32_state) {
+    const size_t bytes = (size_t)c.batch * c.heads * c.dv * c.dk * sizeof(float);
+    const hipError_t e = hipMemcpyAsync(s->state, S_dev, bytes, hipMemcpyDeviceToDevice,
+                                        reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QSTATE_OK : QSTATE_E_LAUNCH;
+  }
+  qs::KParams p = base_params(s);
+  p.src = S_dev;
+  const int rc = run(s, qs::kImport, p, stream);
+  if (rc == QSTATE_OK) ++s->step;
+  return rc;
+}
+
+int qstate_step(qstate* s, const float* q, const float* k, const float* v, const float* alpha,
+                const float* beta, float* o, void* stream) {
+  if (!s || !q || !k || !v || !alpha) return QSTATE_E_INVALID;
+  const qstate_config& c = s->cfg;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 4)) return QSTATE_E_INVALID;
+  if (c.mixer == QSTATE_GLA) {
+    if (!aligned(alpha, 16)) return QSTATE_E_INVALID;
+  } else {
+    if (!beta || !aligned(alpha, 4) || !aligned(beta, 4)) return QSTATE_E_INVALID;
+  }
+  if (o && !aligned(o, 4)) return QSTATE_E_INVALID;
+  qs::KParams p = base_params(s);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = c.mixer == QSTATE_GLA ? nullptr : beta;
+  p.o = o;
+  const int rc = run(s, qs::kStep, p, stream);
+  if (rc == QSTATE_OK) ++s->step;
+  return rc;
+}
+
+int qstate_readout(qstate* s, const float* q, float* o, void* stream) {
+  if (!s || !q || !o || !aligned(q, 16) || !aligned(o, 4)) return QSTATE_E_INVALID;
+  qs::KParams p = base_params(s);
+  p.q = q;
+  p.o = o;
+  return run(s, qs::kReadout, p, stream);
+}
+
+int qstate_store_fp32(qstate* s, float* S_dev, void* stream) {
+  if (!s || !S_dev || !aligned(S_dev, 16)) return QSTATE_E_INVALID;
+  const qstate_config& c = s->cfg;
+  if (c.fp32_state) {
+    const size_t bytes = (size_t)c.batch * c.heads * c.dv * c.dk * sizeof(float);
+    const hipError_t e = hipMemcpyAsync(S_dev, s->state, bytes, hipMemcpyDeviceToDevice,
+                                        reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QSTATE_OK : QSTATE_E_LAUNCH;
+  }
+  qs::KParams p = base_params(s);
+  p.dst = S_dev;
+  return run(s, qs::kExport, p, stream);
+}
+
+int qstate_get_step(const qstate* s, uint64_t* step) {
+  if (!s || !step) return QSTATE_E_INVALID;
+  *step = s->step;
+  return QSTATE_OK;
+}
+
+int qstate_set_step(qstate* s, uint64_t step) {
+  if (!s) return QSTATE_E_INVALID;
+  s->step = step;
+  return QSTATE_OK;
+}
+
+int qstate_destroy(qstate* s) {
+  delete s;
+  return QSTATE_OK;
+}
+
+const char* qstate_strerror(int status) {
+  switch (status) {
+    case QSTATE_OK: return "ok";
+    case QSTATE_E_INVALID: return "invalid argument (null or misaligned pointer, bad size or enum)";
+    case QSTATE_E_UNSUPPORTED: return "unsupported configuration (dk, group, heads or dv)";
+    case QSTATE_E_LAUNCH: return "kernel launch failed";
+    case QSTATE_E_NOMEM: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int qstate_bits_by_decay(const float* retention, int heads, int mode, float thr_or_frac,
+                         uint8_t lo_bits, uint8_t hi_bits, uint8_t* out_bits) {
+  if (!retention || !out_bits || heads < 1) return QSTATE_E_INVALID;
+  if ((lo_bits != 4 && lo_bits != 8) || (hi_bits != 4 && hi_bits != 8)) return QSTATE_E_INVALID;
+  if (mode == 0) {
+    for (int h = 0; h < heads; ++h) out_bits[h] = retention[h] > thr_or_frac ? hi_bits : lo_bits;
+    return QSTATE_OK;
+  }
+  if (mode != 1 || !(thr_or_frac >= 0.0f && thr_or_frac <= 1.0f)) return QSTATE_E_INVALID;
+  const int take = (int)std::floor((double)thr_or_frac * (double)heads + 0.5);
+  // heads ranked by retention, largest first; equal retention keeps index order
+  std::vector<int> rank(heads);
+  std::iota(rank.begin(), rank.end(), 0);
+  std::stable_sort(rank.begin(), rank.end(),
+                   [retention](int a, int b) { return retention[a] > retention[b]; });
+  std::fill(out_bits, out_bits + heads, lo_bits);
+  for (int i = 0; i < take; ++i) out_bits[rank[i]] = hi_bits;
+  return QSTATE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// qstate_launch.h — internal interface between the C ABI (qstate_api.cpp)
+// and the gfx950 kernels (qstate_kernels.hip).  Not installed, not part of
+// the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace qs {
+
+// Everything a kernel needs for one launch, passed by value.
+struct KParams {
+  void* state;           // codes (quantized) or float S (FP32 state)
+  float* scales;         // [B][H][dv][dk/G]
+  const float* q;        // [B][H][dk]
+  const float* k;        // [B][H][dk]
+  const float* v;        // [B][H][dv]
+  const float* alpha;    // [B][H] or [B][H][dk] (GLA)
+  const float* beta;     // [B][H] (GDN, scalar) or null
+  float* o;              // [B][H][dv] or null
+  const float* src;      // import: FP32 state to quantize
+  float* dst;            // export: dequantized FP32 state
+  int32_t B, H, dv, G;
+  uint64_t bytes_per_b;  // code bytes of one batch row (all heads)
+  uint32_t head_bytes4;  // code bytes of an INT4 head = dv*dk/2
+  uint32_t int8_mask[8]; // bit h set: head h stores INT8 codes
+  uint64_t seed;
+  uint32_t layer;
+  uint64_t step;         // stochastic-rounding counter of this event
+};
+
+enum Op { kStep = 0, kImport = 1, kExport = 2, kReadout = 3 };
+
+// Launch one kernel over all B*H heads on `stream`.  Returns hipSuccess or
+// the launch error.  mixer/rounding as in qstate.h; fp32 selects the
+// unquantized-state kernels.
+hipError_t launch(Op op, int mixer, int rounding, int fp32, int dk,
+                  const KParams& p, hipStream_t stream);
+
+}  // namespace qs

@@ -1,0 +1,264 @@
+"""GPU-versus-reference parity harness (used by the gpu tests and the smoke check).
+
+Both sides start from the same seeded inputs (workloads.py) and run the
+whole workload independently: FP32 warm-up steps, the FP32 import, then the
+quantized decode steps.  The CPU reference runs per head, so any subset of
+the heads of a full-size batch can be checked one by one.
+
+Contract per checked step and head:
+  * codes bit-equal, except elements whose pre-rounding value lies within
+    1e-6 (in code units) of a rounding threshold; those are counted, must be
+    below 1e-5 of all checked elements, and the GPU head is then re-synced
+    from the reference state (reference -> GPU only);
+  * scales bit-equal;
+  * o and the dequantized state within |a - b| <= 1e-5 + 1e-4 |b|;
+  * the FP32 warm-up state bit-equal (the unquantized run is the FP32
+    recurrence).
+"""
+
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+from bit_recurrent_state_amd import qstate as Q
+
+ATOL, RTOL = 1e-5, 1e-4
+NEAR = 1e-6
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits_rule(w: W.Workload):
+    """(mode, threshold-or-fraction) of the decay-based allocation for w."""
+    if w.bits_policy == "alpha_gt_0.99":
+        return 0, 0.99
+    if w.bits_policy == "rank_half":
+        return 1, 0.5
+    return None
+
+
+def head_bits(w: W.Workload, seed=0, layer=0):
+    """Per-head bits from the library and from the reference, which must agree."""
+    rule = bits_rule(w)
+    if rule is None:
+        return np.full(w.H, 8, np.uint8)
+    ret = W.head_retention(w, seed, layer)
+    lib_bits = Q.qstate_bits_by_decay(ret, rule[0], rule[1])
+    ref_bits = oracle.bits_by_decay(ret, rule[0], rule[1])
+    assert np.array_equal(lib_bits, ref_bits), (lib_bits, ref_bits)
+    return lib_bits
+
+
+@dataclass
+class Report:
+    steps: int = 0
+    elements: int = 0
+    exempt: int = 0
+    resyncs: int = 0
+    max_o_err: float = 0.0
+    max_s_err: float = 0.0
+    first_exempt_step: int = -1
+    notes: list = field(default_factory=list)
+
+
+def _to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def _close(a, b):
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    err = np.abs(a64 - b64)
+    return bool(np.all(err <= ATOL + RTOL * np.abs(b64))), float(err.max() if err.size else 0.0)
+
+
+def _inputs_dev(inp):
+    return [None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in inp]
+
+
+class Run:
+    """One workload instance on both sides."""
+
+    def __init__(self, w: W.Workload, rounding=None, seed=0, layer=0, heads=None,
+                 fp32_only=False, head_bits_override=None):
+        self.w = w
+        self.rounding = w.rounding if rounding is None else rounding
+        self.seed, self.layer = seed, layer
+        if head_bits_override is not None:
+            self.hb = np.asarray(head_bits_override, np.uint8)
+        else:
+            self.hb = head_bits(w, seed, layer)
+        self.cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, False,
+                            [int(x) for x in self.hb], seed, layer)
+        self.ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, seed, layer)
+        all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        self.heads = all_heads if heads is None else list(heads)
+        self.rep = Report()
+        self.t_in = 0  # next input step index
+        self.fp32_only = fp32_only
+
+    # ---- helpers -----------------------------------------------------------------
+    def inputs(self, t):
+        return W.step_inputs(self.w, t, self.seed, self.layer)
+
+    def head_codes_slice(self, b, h):
+        off = oracle.head_offset(self.ocfg, b, h, self.hb)
+        n = self.w.dv * self.w.dk * int(self.hb[h]) // 8
+        return off, n
+
+    def _alpha_head(self, alpha, b, h):
+        return alpha[b, h] if self.w.mixer == W.GLA else np.float32([alpha[b, h]])
+
+    def _beta_head(self, beta, b, h):
+        return 0.0 if beta is None else float(beta[b, h])
+
+    # ---- phases ------------------------------------------------------------------
+    def warmup_and_import(self):
+        w = self.w
+        zeros = torch.zeros(w.B * w.H * w.dv * w.dk, dtype=torch.float32, device="cuda")
+        fcfg = Q.Config(w.B, w.H, w.dk, w.dv, 16, w.mixer, 0, True, None, self.seed, self.layer)
+        f = Q.QState(fcfg)
+        f.load_fp32(zeros)
+        S_ref = {bh: np.zeros((w.dv, w.dk), np.float32) for bh in self.heads}
+        for t in range(w.warmup):
+            q, k, v, alpha, beta = self.inputs(t)
+            dq, dk_, dv_, da, db = _inputs_dev((q, k, v, alpha, beta))
+            f.step(dq, dk_, dv_, da, db, None)
+            for (b, h) in self.heads:
+                oracle.head_step_fp32(self.ocfg, S_ref[(b, h)], q[b, h], k[b, h], v[b, h],
+                                      self._alpha_head(alpha, b, h), self._beta_head(beta, b, h))
+        self.t_in = w.warmup
+        S_gpu = torch.empty_like(zeros)
+        f.store_fp32(S_gpu)
+        torch.cuda.synchronize()
+        Sg = _to_np(S_gpu).reshape(w.B, w.H, w.dv, w.dk)
+        for (b, h) in self.heads:
+            if not np.array_equal(Sg[b, h].view(np.uint32), S_ref[(b, h)].view(np.uint32)):
+                bad = np.argwhere(Sg[b, h] != S_ref[(b, h)])
+                raise AssertionError(f"FP32 warm-up state differs at head {(b, h)}, "
+                                     f"{len(bad)} elements, first {bad[:3].tolist()}")
+        f.close()
+        self.S_fp32_ref = S_ref
+        if self.fp32_only:
+            return
+        self.gpu = Q.QState(self.cfg)
+        self.gpu.load_fp32(S_gpu)  # counter 0 -> 1
+        self.ref, xvals = {}, {}
+        for (b, h) in self.heads:
+            codes, scales, xv = oracle.head_quantize(self.ocfg, b, h, int(self.hb[h]),
+                                                     S_ref[(b, h)], 0, want_xval=True)
+            self.ref[(b, h)] = (codes, scales)
+            xvals[(b, h)] = xv
+        torch.cuda.synchronize()
+        self.compare(step=0, o_gpu=None, o_ref=None, xvals=xvals)
+
+    def step(self, check=True):
+        w = self.w
+        q, k, v, alpha, beta = self.inputs(self.t_in)
+        self.t_in += 1
+        counter = self.gpu.step_counter
+        dq, dk_, dv_, da, db = _inputs_dev((q, k, v, alpha, beta))
+        o_dev = torch.full((w.B * w.H * w.dv,), float("nan"), dtype=torch.float32, device="cuda")
+        self.gpu.step(dq, dk_, dv_, da, db, o_dev)
+        o_ref, xvals = {}, {}
+        for (b, h) in self.heads:
+            codes, scales = self.ref[(b, h)]
+            o, _, xv = oracle.head_step(self.ocfg, b, h, int(self.hb[h]), codes, scales, q[b, h],
+                                        k[b, h], v[b, h], self._alpha_head(alpha, b, h),
+                                        self._beta_head(beta, b, h), counter, want_xval=True)
+            o_ref[(b, h)] = o
+            xvals[(b, h)] = xv
+        torch.cuda.synchronize()
+        if check:
+            self.compare(step=counter, o_gpu=_to_np(o_dev).reshape(w.B, w.H, w.dv), o_ref=o_ref,
+                         xvals=xvals)
+        self.rep.steps += 1
+
+    def compare(self, step, o_gpu, o_ref, xvals=None):
+        w = self.w
+        codes_g = _to_np(self.gpu.codes)
+        scales_g = _to_np(self.gpu.scales).reshape(w.B, w.H, w.dv, w.dk // w.G)
+        for (b, h) in self.heads:
+            bits = int(self.hb[h])
+            off, n = self.head_codes_slice(b, h)
+            cg = codes_g[off:off + n]
+            cr, sr = self.ref[(b, h)]
+            self.rep.elements += w.dv * w.dk
+            if not np.array_equal(scales_g[b, h].ravel().view(np.uint32), sr.view(np.uint32)):
+                bad = np.argwhere(scales_g[b, h].ravel() != sr)
+                raise AssertionError(f"step {step} head {(b, h)}: {len(bad)} scales differ, "
+                                     f"first {bad[:4].ravel().tolist()}")
+            if not np.array_equal(cg, cr):
+                self._exempt_or_fail(step, b, h, bits, cg, cr, xvals)
+            if o_gpu is not None:
+                ok, err = _close(o_gpu[b, h], o_ref[(b, h)])
+                self.rep.max_o_err = max(self.rep.max_o_err, err)
+                if not ok:
+                    raise AssertionError(f"step {step} head {(b, h)}: o differs, max err {err}")
+        if self.rep.exempt > max(1e-5 * self.rep.elements, 0):
+            raise AssertionError(f"{self.rep.exempt} near-threshold exemptions in "
+                                 f"{self.rep.elements} elements")
+
+    def _exempt_or_fail(self, step, b, h, bits, cg, cr, xvals):
+        w = self.w
+        a = _decode(cg, bits)
+        r = _decode(cr, bits)
+        bad = np.nonzero(a != r)[0]
+        x = xvals[(b, h)].ravel()[bad]
+        if self.rounding == W.SR:
+            dist = np.abs(x - np.rint(x))
+        else:
+            dist = np.abs(x - (np.floor(x) + 0.5))
+        if np.any(dist >= NEAR) or np.any(np.abs(a[bad] - r[bad]) != 1):
+            i = bad[np.argmax(dist)]
+            raise AssertionError(f"step {step} head {(b, h)}: {len(bad)} codes differ, element "
+                                 f"{i} gpu {a[i]} ref {r[i]} pre-rounding {xvals[(b, h)].ravel()[i]}")
+        self.rep.exempt += len(bad)
+        if self.rep.first_exempt_step < 0:
+            self.rep.first_exempt_step = step
+        # re-sync the GPU head from the reference (reference -> GPU only)
+        off, n = self.head_codes_slice(b, h)
+        self.gpu.codes[off:off + n] = torch.from_numpy(cr).cuda()
+        self.rep.resyncs += 1
+
+    def dequant_check(self):
+        """Export (dequantized state) and readout against the reference."""
+        w = self.w
+        S = torch.empty(w.B * w.H * w.dv * w.dk, dtype=torch.float32, device="cuda")
+        self.gpu.store_fp32(S)
+        q, *_ = self.inputs(self.t_in)
+        o = torch.empty(w.B * w.H * w.dv, dtype=torch.float32, device="cuda")
+        self.gpu.readout(torch.from_numpy(q).cuda(), o)
+        torch.cuda.synchronize()
+        Sg = _to_np(S).reshape(w.B, w.H, w.dv, w.dk)
+        og = _to_np(o).reshape(w.B, w.H, w.dv)
+        for (b, h) in self.heads:
+            codes, scales = self.ref[(b, h)]
+            Sr = oracle.head_dequantize(self.ocfg, int(self.hb[h]), codes, scales)
+            assert np.array_equal(Sg[b, h], Sr), f"export differs at head {(b, h)}"
+            orr = oracle.head_readout(self.ocfg, int(self.hb[h]), codes, scales, q[b, h])
+            ok, err = _close(og[b, h], orr)
+            assert ok, f"readout differs at head {(b, h)}: {err}"
+            self.rep.max_s_err = max(self.rep.max_s_err, float(np.abs(Sg[b, h] - Sr).max()))
+
+    def close(self):
+        if hasattr(self, "gpu"):
+            self.gpu.close()
+
+
+def _decode(codes: np.ndarray, bits: int) -> np.ndarray:
+    if bits == 8:
+        return codes.view(np.int8).astype(np.int32)
+    x = np.empty(codes.size * 2, np.int32)
+    x[0::2] = codes & 0xF
+    x[1::2] = codes >> 4
+    x[x >= 8] -= 16
+    return x

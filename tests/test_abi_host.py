@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point of include/qstate.h, and validates its arguments before
+touching a device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_recurrent_state_amd import build
+    if build.stale():
+        build.build()
+    from bit_recurrent_state_amd._lib import lib
+    return lib()
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "qstate.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(qstate_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _header_functions()
+    assert len(names) >= 11
+    from bit_recurrent_state_amd._lib import EXPORTS
+    assert sorted(EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _cfg(**kw):
+    from bit_recurrent_state_amd._lib import QStateConfig
+    base = dict(batch=2, heads=3, dk=128, dv=64, group=32, mixer=0, rounding=1, fp32_state=0,
+                head_bits=None, seed=1, layer=2)
+    base.update(kw)
+    return QStateConfig(**base)
+
+
+def _bits(*b):
+    arr = (ctypes.c_uint8 * len(b))(*b)
+    return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8))
+
+
+def test_state_bytes(L):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    keep, hb = _bits(4, 8, 4)
+    c = _cfg(head_bits=hb)
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 2 * 64 * 128 * (4 + 8 + 4) // 8
+    assert sb.value == 2 * 3 * 64 * (128 // 32) * 4
+    c = _cfg(fp32_state=1)
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 2 * 3 * 64 * 128 * 4 and sb.value == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -1), (dict(heads=0), -1), (dict(dv=0), -1), (dict(mixer=3), -1),
+    (dict(rounding=2), -1), (dict(group=48), -1), (dict(fp32_state=2), -1),
+    (dict(dk=96, group=32), -2), (dict(dk=512, group=64), -2), (dict(heads=300), -2),
+    (dict(dv=5000), -2), (dict(group=8), -2),
+])
+def test_invalid_configs_rejected(L, kw, status):
+    c = _cfg(**kw)
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == status
+    h = ctypes.c_void_p()
+    assert L.qstate_create(ctypes.byref(c), ctypes.c_void_p(4096), ctypes.c_void_p(8192),
+                           ctypes.byref(h)) == status
+    assert h.value is None
+
+
+def test_bad_head_bits_and_pointers(L):
+    keep, hb = _bits(4, 6, 8)
+    c = _cfg(head_bits=hb)
+    h = ctypes.c_void_p()
+    assert L.qstate_create(ctypes.byref(c), ctypes.c_void_p(4096), ctypes.c_void_p(8192),
+                           ctypes.byref(h)) == -1
+    c = _cfg()
+    for codes, scales in ((0, 8192), (4096, 0), (4100, 8192), (4096, 8196)):
+        assert L.qstate_create(ctypes.byref(c), ctypes.c_void_p(codes or None),
+                               ctypes.c_void_p(scales or None), ctypes.byref(h)) == -1
+
+
+def test_handle_lifecycle_and_argument_checks(L):
+    """Create (host only), counters, and synchronous rejection of bad step
+    arguments: none of these reach the device."""
+    c = _cfg()
+    h = ctypes.c_void_p()
+    assert L.qstate_create(ctypes.byref(c), ctypes.c_void_p(4096), ctypes.c_void_p(8192),
+                           ctypes.byref(h)) == 0
+    step = ctypes.c_uint64()
+    assert L.qstate_get_step(h, ctypes.byref(step)) == 0 and step.value == 0
+    assert L.qstate_set_step(h, 41) == 0
+    assert L.qstate_get_step(h, ctypes.byref(step)) == 0 and step.value == 41
+    P = ctypes.c_void_p
+    ok = P(1 << 20)
+    # null q, misaligned k, missing beta for GDN
+    assert L.qstate_step(h, None, ok, ok, ok, ok, None, None) == -1
+    assert L.qstate_step(h, ok, P((1 << 20) + 4), ok, ok, ok, None, None) == -1
+    assert L.qstate_step(h, ok, ok, ok, ok, None, None, None) == -1
+    assert L.qstate_readout(h, ok, None, None) == -1
+    assert L.qstate_load_fp32(h, P((1 << 20) + 8), None) == -1
+    assert L.qstate_store_fp32(h, None, None) == -1
+    assert L.qstate_get_step(h, ctypes.byref(step)) == 0 and step.value == 41  # unchanged
+    assert L.qstate_destroy(h) == 0
+    assert L.qstate_destroy(None) == 0
+    assert L.qstate_strerror(0) == b"ok"
+    assert L.qstate_strerror(-2).startswith(b"unsupported")
+
+
+def test_bits_by_decay_matches_rules(L):
+    from bit_recurrent_state_amd.qstate import qstate_bits_by_decay
+    ret = np.array([0.95, 0.995, 0.991, 0.99, 0.90, 0.999], np.float32)
+    assert qstate_bits_by_decay(ret, 0, 0.99).tolist() == [4, 8, 8, 4, 4, 8]
+    ret = np.array([0.5, 0.9, 0.7, 0.9, 0.1, 0.7], np.float32)
+    assert qstate_bits_by_decay(ret, 1, 0.5).tolist() == [4, 8, 8, 8, 4, 4]
+    with pytest.raises(Exception):
+        qstate_bits_by_decay(ret, 1, 1.5)
+
+
+def test_bits_by_decay_agrees_with_reference(L, oracle):
+    from bit_recurrent_state_amd.qstate import qstate_bits_by_decay
+    rng = np.random.default_rng(5)
+    for _ in range(100):
+        ret = rng.choice([0.1, 0.5, 0.9, 0.95, 0.99, 0.999], 32).astype(np.float32)
+        for mode, arg in ((0, 0.99), (1, 0.5), (1, 0.25)):
+            assert np.array_equal(qstate_bits_by_decay(ret, mode, arg),
+                                  oracle.bits_by_decay(ret, mode, arg))
+
+
+def test_product_package_does_not_use_the_reference():
+    """The product path never imports, links or loads the CPU reference."""
+    pkg = os.path.join(ROOT, "bit_recurrent_state_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU reference.
+
+Every case runs the whole workload on both sides from the same seeded
+inputs; see tests/parity.py for the comparison contract."""
+
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a gfx950 GPU")]
+
+if gpu_available():
+    import torch
+
+    import oracle
+    import workloads as W
+    from bit_recurrent_state_amd import qstate as Q
+    from parity import Run, log
+else:  # keep collection working on CPU-only hosts
+    import workloads as W
+
+
+def _run(w, steps, rounding=None, heads=None, seed=0, layer=0, hb=None):
+    r = Run(w, rounding, seed, layer, heads, head_bits_override=hb)
+    log(f"[case] {w.name} B={w.B} H={w.H} dk={w.dk} dv={w.dv} G={w.G} mixer={w.mixer} "
+        f"rounding={r.rounding} bits={sorted(set(r.hb.tolist()))} warmup={w.warmup} "
+        f"steps={steps} heads={len(r.heads)} seed={seed} layer={layer}")
+    r.warmup_and_import()
+    for _ in range(steps):
+        r.step()
+    r.dequant_check()
+    r.close()
+    log(f"[done] steps={r.rep.steps} elements={r.rep.elements} exempt={r.rep.exempt} "
+        f"max_o_err={r.rep.max_o_err:.3g}")
+    return r.rep
+
+
+def test_config0_every_step_every_head():
+    rep = _run(W.WORKLOADS[0], W.WORKLOADS[0].steps)
+    assert rep.exempt == 0
+
+
+def test_config1_int8_sr_every_head():
+    _run(W.WORKLOADS[1].scaled(B=4), 24)
+
+
+def test_config2_int4_int8_mix_every_head():
+    w = W.WORKLOADS[2].scaled(B=2)
+    from parity import head_bits
+    hb = head_bits(w)
+    assert 4 in hb and 8 in hb  # the decay rule gives a real mix
+    _run(w, 12)
+
+
+@pytest.mark.parametrize("rounding", [W.RTN, W.SR])
+def test_config3_gla_every_head(rounding):
+    _run(W.WORKLOADS[3].scaled(B=3), 10, rounding=rounding)
+
+
+@pytest.mark.parametrize("layer", [0, 5])
+def test_config4_scalar_decay_layers(layer):
+    _run(W.WORKLOADS[4].scaled(B=3), 8, layer=layer)
+
+
+# ragged and edge shapes: dv not a multiple of the rows per iteration, all dk,
+# all group sizes, mixed bits in any order, every recurrence and rounding
+RAGGED = [
+    (W.GDN, W.SR, 64, 37, 16, [8, 4, 4, 8, 4]),
+    (W.GDN, W.RTN, 256, 21, 128, [4, 8, 4]),
+    (W.GLA, W.SR, 128, 45, 32, [4, 4, 8]),
+    (W.SCALAR, W.RTN, 128, 1, 64, [8, 4]),
+    (W.SCALAR, W.SR, 256, 70, 16, [4, 8]),
+    (W.GDN, W.SR, 128, 129, 128, [4]),
+]
+
+
+@pytest.mark.parametrize("mixer,rounding,dk,dv,G,bits", RAGGED)
+def test_ragged_shapes(mixer, rounding, dk, dv, G, bits):
+    w = W.Workload(90 + mixer, f"ragged_m{mixer}_dk{dk}_dv{dv}_g{G}", mixer, 3, len(bits), dk, dv,
+                   G, 6, 4, rounding, "int8")
+    _run(w, 6, hb=np.array(bits, np.uint8), seed=7)
+
+
+@pytest.mark.parametrize("mixer", [W.GDN, W.GLA, W.SCALAR])
+def test_fp32_state_is_the_fp32_recurrence(mixer):
+    """The unquantized run equals the reference FP32 recurrence bit for bit."""
+    w = W.Workload(95, f"fp32_m{mixer}", mixer, 4, 8, 128, 128, 32, 0, 48, W.RTN, "int8")
+    r = Run(w, fp32_only=True)
+    log(f"[case] fp32 mixer={mixer} warmup={w.warmup}")
+    r.warmup_and_import()
+
+
+FULL = {1: 3, 2: 2, 3: 2, 4: 2}
+
+
+@pytest.mark.parametrize("wid", sorted(FULL))
+def test_full_size_sampled_heads(wid):
+    """Full-size launch (the benchmark's shapes); a seeded sample of heads is
+    checked against the reference at every step."""
+    w = W.WORKLOADS[wid]
+    rng = np.random.default_rng(wid)
+    idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
+    heads = sorted((i // w.H, i % w.H) for i in idx)
+    _run(w, FULL[wid], heads=heads)
+
+
+def _small_case(mixer=W.GDN, rounding=W.SR, bits=(4, 8, 8)):
+    return W.Workload(97, "small", mixer, 2, len(bits), 128, 48, 32, 6, 3, rounding, "int8"), \
+        np.array(bits, np.uint8)
+
+
+def _dev(x):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def test_resume_is_bit_exact():
+    """The quantized state is the checkpoint: codes + scales + step counter."""
+    w, hb = _small_case()
+    cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 3, 1)
+    rng = np.random.default_rng(3)
+    S0 = torch.from_numpy(rng.standard_normal(w.B * w.H * w.dv * w.dk).astype(np.float32)).cuda()
+    a = Q.QState(cfg)
+    a.load_fp32(S0)
+    steps = [W.step_inputs(w, t) for t in range(6)]
+    for t in range(3):
+        a.step(*map(_dev, steps[t]))
+    codes, scales, counter = a.codes.clone(), a.scales.clone(), a.step_counter
+    outs_a = []
+    for t in range(3, 6):
+        o = torch.empty(w.B * w.H * w.dv, device="cuda")
+        a.step(*map(_dev, steps[t]), o)
+        outs_a.append(o.cpu())
+    b = Q.QState(cfg)
+    b.codes.copy_(codes)
+    b.scales.copy_(scales)
+    b.step_counter = counter
+    for t in range(3, 6):
+        o = torch.empty(w.B * w.H * w.dv, device="cuda")
+        b.step(*map(_dev, steps[t]), o)
+        assert torch.equal(o.cpu(), outs_a[t - 3])
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    assert a.step_counter == b.step_counter == 7
+
+
+def test_guard_bytes_untouched():
+    """In-place updates stay inside the caller's buffers."""
+    w, hb = _small_case(bits=(4, 8))
+    cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0, 0)
+    cb, sb = Q.qstate_state_bytes(cfg)
+    pad = 4096
+    cbuf = torch.full((cb + 2 * pad,), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((sb // 4 + 2 * pad,), 7.25, dtype=torch.float32, device="cuda")
+    obuf = torch.full((w.B * w.H * w.dv + 2 * pad,), 3.5, dtype=torch.float32, device="cuda")
+    codes, scales = cbuf[pad:pad + cb], sbuf[pad:pad + sb // 4]
+    o = obuf[pad:pad + w.B * w.H * w.dv]
+    h = Q.qstate_create(cfg, codes, scales)
+    S0 = torch.randn(w.B * w.H * w.dv * w.dk, device="cuda")
+    Q.qstate_load_fp32(h, S0, cfg)
+    for t in range(4):
+        q, k, v, alpha, beta = map(_dev, W.step_inputs(w, t))
+        Q.qstate_step(h, cfg, q, k, v, alpha, beta, o)
+    Q.qstate_readout(h, cfg, q, o)
+    torch.cuda.synchronize()
+    Q.qstate_destroy(h)
+    assert torch.all(cbuf[:pad] == 0xAB) and torch.all(cbuf[pad + cb:] == 0xAB)
+    assert torch.all(sbuf[:pad] == 7.25) and torch.all(sbuf[pad + sb // 4:] == 7.25)
+    assert torch.all(obuf[:pad] == 3.5) and torch.all(obuf[-pad:] == 3.5)
+
+
+def test_nan_in_one_row_stays_in_its_head():
+    """Heads are independent: a NaN in one head's v leaves every other head
+    bit-identical to a clean run."""
+    w, hb = _small_case(mixer=W.GDN, bits=(8, 4, 8))
+    cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 1, 0)
+    S0 = torch.randn(w.B * w.H * w.dv * w.dk, device="cuda", generator=None)
+    runs = []
+    for poison in (False, True):
+        a = Q.QState(cfg)
+        a.load_fp32(S0)
+        for t in range(3):
+            q, k, v, alpha, beta = W.step_inputs(w, t)
+            if poison and t == 1:
+                v = v.copy()
+                v[1, 1, 5] = np.nan
+            a.step(*map(_dev, (q, k, v, alpha, beta)))
+        torch.cuda.synchronize()
+        runs.append((a.codes.cpu().numpy(), a.scales.cpu().numpy().reshape(w.B, w.H, -1)))
+    ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G)
+    off = oracle.head_offset(ocfg, 1, 1, hb)
+    n = w.dv * w.dk * int(hb[1]) // 8
+    keep = np.ones(runs[0][0].size, bool)
+    keep[off:off + n] = False
+    assert np.array_equal(runs[0][0][keep], runs[1][0][keep])
+    sk = np.ones((w.B, w.H), bool)
+    sk[1, 1] = False
+    assert np.array_equal(runs[0][1][sk], runs[1][1][sk])
+
+
+def test_zero_state_stays_zero():
+    w, hb = _small_case(bits=(4, 8))
+    for rounding in (W.RTN, W.SR):
+        cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, rounding, False, hb.tolist(), 0, 0)
+        a = Q.QState(cfg)
+        a.load_fp32(torch.zeros(w.B * w.H * w.dv * w.dk, device="cuda"))
+        q, k, v, alpha, beta = W.step_inputs(w, 0)
+        o = torch.full((w.B * w.H * w.dv,), 1.0, device="cuda")
+        a.step(*map(_dev, (q, k, np.zeros_like(v), alpha, beta)), o)
+        torch.cuda.synchronize()
+        assert torch.all(a.codes == 0) and torch.all(a.scales == 0) and torch.all(o == 0)
