@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kMaxHeads = 256;
 constexpr int kMaxDv = 4096;
+constexpr int64_t kTargetWaves = 4096;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -51,7 +52,8 @@ int check_config(const qstate_config* c) {
     return QSTATE_E_UNSUPPORTED;
   // every index the kernels form must stay inside 63-bit sizes and a 32-bit grid
   const double elems = (double)c->batch * c->heads * c->dv * c->dk;
-  if (elems * 4.0 > 9.0e18 || (double)c->batch * c->heads > 2147483647.0) return QSTATE_E_UNSUPPORTED;
+  if (elems * 4.0 > 9.0e18 || (double)c->batch * c->heads * ((c->dv + 31) / 32) > 2147483647.0)
+    return QSTATE_E_UNSUPPORTED;
   return QSTATE_OK;
 }
 
@@ -82,6 +84,15 @@ qs::KParams base_params(const qstate* s) {
   p.H = s->cfg.heads;
   p.dv = s->cfg.dv;
   p.G = s->cfg.fp32_state ? 16 : s->cfg.group;
+  // One wave per row slice: split heads until the launch has at least
+  // kTargetWaves waves (16 per CU on 256 CUs), in slices of whole 32-row units.
+  const int64_t heads = (int64_t)s->cfg.batch * s->cfg.heads;
+  const int units = (s->cfg.dv + 31) / 32;
+  int slices = (int)std::min<int64_t>((kTargetWaves + heads - 1) / heads, units);
+  slices = std::max(slices, 1);
+  const int units_per_slice = (units + slices - 1) / slices;
+  p.slice_rows = 32 * units_per_slice;
+  p.slices = (units + units_per_slice - 1) / units_per_slice;
   p.bytes_per_b = s->bytes_per_b;
   p.head_bytes4 = (uint32_t)((uint64_t)s->cfg.dv * s->cfg.dk / 2);
   std::memcpy(p.int8_mask, s->int8_mask, sizeof(p.int8_mask));

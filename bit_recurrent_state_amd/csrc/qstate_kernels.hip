@@ -1,21 +1,37 @@
 // qstate_kernels.hip — fused quantized recurrent-state decode kernels, gfx950.
 //
-// One workgroup (4 x wave64) owns one head (b, h).  A value row of the state
-// is split into 16-element chunks, one per lane, so a row of dk columns spans
-// LPR = dk/16 adjacent lanes and a wave holds 64/LPR rows at a time.  Every
-// operation of the step is row-local (LoReS blog, "LoReS: State
-// Quantization": value-axis groups, full-precision update, readout from the
-// updated state): the two dot products u = d.k and o = S'.q finish with an
-// xor butterfly over the row's lanes, and the group absmax with a butterfly
-// over the G/16 lanes of the group.  No LDS, no atomics, no cross-workgroup
-// traffic: each state byte is read once and written once per step.
+// One wave (a workgroup of 64 lanes) owns a slice of the rows of one head
+// (b, h); small batches split a head into several slices so that enough
+// waves exist to fill 256 CUs.  A value row of the state is split across
+// adjacent lanes: each lane owns one 16-byte run of codes, i.e. 16 INT8
+// elements or 32 INT4 elements, so a row of dk columns spans dk/16 (INT8) or
+// dk/32 (INT4) lanes and the wave holds the rest of its 64 lanes as further
+// rows.  The loads of the next kPrefetch row iterations are in flight while
+// the current one is computed.  Every operation of the step is row-local (LoReS
+// blog, "LoReS: State Quantization": value-axis groups, full-precision update,
+// readout from the updated state): the two dot products u = d.k and o = S'.q
+// finish with DPP butterflies across the row's lanes, the group absmax with
+// DPP butterflies across the group's lanes.  No LDS, no atomics, no
+// cross-workgroup traffic: each state byte is read once and written once.
 //
 // Arithmetic follows the semantics written in include/qstate.h operation by
 // operation (explicit fmaf, no contraction, IEEE division), so the stored
 // codes are bit-identical to any other implementation of those semantics.
-// The per-lane 16-element chunk and the butterfly realise the summation
-// order defined there: sequential fused multiply-adds inside a chunk, then a
-// pairwise tree over chunks (xor 1, 2, 4, ... pairs adjacent partials).
+// The 16-element chunks and the butterflies realise the summation order
+// defined there: sequential fused multiply-adds inside a chunk, then a
+// pairwise tree over the chunks (an INT4 lane adds its two adjacent chunks,
+// then DPP pairs adjacent lanes, adjacent lane pairs, ...).
+//
+// Instruction economy (the INT4 + stochastic-rounding path is VALU-bound):
+//  * codes are turned into floats with v_cvt_f32_ubyte after flipping the
+//    sign bit of each byte/nibble (offset binary c + 2^(n-1)); the decayed
+//    value c*sa is then one fma(cu, sa, -2^(n-1)*sa), which is exactly the
+//    rounded product c*sa because the addend is exact;
+//  * stochastic rounding evaluates floor(S'*inv + R/2^16) as
+//    floor(fma(S', inv*2^16, R) / 2^16): the scaling by 2^16 is exact, so the
+//    code is byte 2 of floor(fma(...)), gathered with v_perm_b32;
+//  * round-to-nearest adds 1.5*2^23 inside the fma, which leaves the rounded
+//    code in the low byte of the result.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,10 +41,8 @@
 namespace qs {
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves of 64
-constexpr int kChunk = 16;     // row elements per lane
-constexpr int kBatch = 4;      // row iterations whose loads are in flight together
-
+constexpr int kThreads = 64;  // one wave per workgroup
+constexpr int kPrefetch = 4;  // row iterations whose loads are in flight ahead of compute
 constexpr int kGDN = 0, kGLA = 1, kScalar = 2;
 
 // ---------------------------------------------------------------------------
@@ -71,41 +85,69 @@ __device__ __forceinline__ uint32_t xorshift32(uint32_t y) {
   return y;
 }
 
-// The 16 stochastic-rounding uniforms of one lane's chunk: the chunk is
-// exactly one 16-element block of the head, so one hashed seed and a walk of
-// seven xorshift32 steps give its eight 32-bit words.
-__device__ __forceinline__ void chunk_uniforms(uint32_t key, uint32_t block, float (&u)[kChunk]) {
+// The 16 random 16-bit values R of one 16-element block, as floats: one
+// hashed seed and a walk of seven xorshift32 steps give the block's eight
+// 32-bit words (low half: even element, high half: odd element).
+__device__ __forceinline__ void block_r16(uint32_t key, uint32_t block, float* r) {
   uint32_t w = fmix32(key ^ block);
   w = w > 1u ? w : 1u;
 #pragma unroll
-  for (int pr = 0; pr < kChunk / 2; ++pr) {
+  for (int pr = 0; pr < 8; ++pr) {
     if (pr) w = xorshift32(w);
-    u[2 * pr] = (float)(w & 0xFFFFu) * (1.0f / 65536.0f);
-    u[2 * pr + 1] = (float)(w >> 16) * (1.0f / 65536.0f);
+    r[2 * pr] = (float)(w & 0xFFFFu);
+    r[2 * pr + 1] = (float)(w >> 16);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Cross-lane reductions inside a row / a group (wave64 xor butterflies).
+// DPP butterflies inside a 16-lane row of the wave.  After the two quad
+// levels every lane of a quad holds the quad's value, so the half-row mirror
+// pairs quad 0 with quad 1 and the row mirror pairs the two halves: each
+// level adds adjacent partials of the tree, as xor butterflies would.
 // ---------------------------------------------------------------------------
 
-template <int LPR>
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int LANES>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) x = x + __shfl_xor(x, off);
+  if constexpr (LANES >= 2) x = x + dpp<kDppXor1>(x);
+  if constexpr (LANES >= 4) x = x + dpp<kDppXor2>(x);
+  if constexpr (LANES >= 8) x = x + dpp<kDppHalfMirror>(x);
+  if constexpr (LANES >= 16) x = x + dpp<kDppMirror>(x);
   return x;
 }
 
-__device__ __forceinline__ float group_max(float m, int lanes_per_group) {
-  for (int off = 1; off < lanes_per_group; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+template <int LANES>
+__device__ __forceinline__ float lanes_max(float m) {
+  if constexpr (LANES >= 2) m = fmaxf(m, dpp<kDppXor1>(m));
+  if constexpr (LANES >= 4) m = fmaxf(m, dpp<kDppXor2>(m));
+  if constexpr (LANES >= 8) m = fmaxf(m, dpp<kDppHalfMirror>(m));
   return m;
 }
 
-// Sequential fused dot product of one 16-element chunk, from +0.
-__device__ __forceinline__ float chunk_dot(const float (&x)[kChunk], const float (&y)[kChunk]) {
+// Sequential fused dot product of the 16-element chunk starting at x[off].
+template <int N>
+__device__ __forceinline__ float chunk_dot(const float (&x)[N], const float (&y)[N], int off) {
   float acc = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j) acc = __builtin_fmaf(x[j], y[j], acc);
+  for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(x[off + j], y[off + j], acc);
+  return acc;
+}
+
+// Lane partial of a row dot product: the lane's chunks summed in order.
+template <int N>
+__device__ __forceinline__ float lane_dot(const float (&x)[N], const float (&y)[N]) {
+  float acc = chunk_dot(x, y, 0);
+  if constexpr (N == 32) acc = acc + chunk_dot(x, y, 16);
   return acc;
 }
 
@@ -114,107 +156,151 @@ __device__ __forceinline__ float chunk_dot(const float (&x)[kChunk], const float
 // float with inv * m <= r); an all-zero group gets s = inv = 0.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void group_scale(float m, float r, float& s, float& inv) {
-  s = m / r;
+// s = m / r, correctly rounded, as one product and one fused correction:
+// with c = RN(1/r), q = m*c, e = fma(-q, r, m), fma(e, c, q) equals RN(m/r)
+// for every normal m when r is 7 or 127 (an exhaustive check over all
+// mantissas is part of the tests); tiny m keeps the IEEE division.
+template <int R>
+__device__ __forceinline__ void group_scale(float m, float& s, float& inv) {
+  constexpr float r = (float)R;
+  constexpr float c = 1.0f / (float)R;
+  const float q = m * c;
+  s = __builtin_fmaf(__builtin_fmaf(-q, r, m), c, q);
+  if (__builtin_expect(m < 0x1p-100f && m != 0.0f, 0)) s = m / r;
   float v = r / m;
   if (__builtin_fmaf(m, v, -r) > 0.0f) v = __int_as_float(__float_as_int(v) - 1);
   inv = (m == 0.0f) ? 0.0f : v;
 }
 
 // ---------------------------------------------------------------------------
-// Code chunks: INT8 = 16 bytes (4 dwords), INT4 = 8 bytes (2 dwords, even
-// element in the low nibble).  Codes are two's complement.
+// Lane geometry: one 16-byte run of codes per lane.
 // ---------------------------------------------------------------------------
 
-template <int BITS>
-struct Codes {
-  uint32_t w[BITS / 2];
+template <int DK, int BITS>
+struct Geo {
+  static constexpr int E = BITS == 4 ? 32 : 16;  // elements per lane
+  static constexpr int LPR = DK / E;             // lanes per row
+  static constexpr int RPW = 64 / LPR;           // rows per wave iteration
+  static constexpr int ROW_BYTES = DK * BITS / 8;
 };
 
+// Codes to floats in offset binary: cu = c + 2^(BITS-1).  16 elements from
+// four words (INT8) or two words (INT4).
 template <int BITS>
-__device__ __forceinline__ Codes<BITS> load_codes(const uint8_t* ptr) {
-  Codes<BITS> c;
-  if constexpr (BITS == 8) {
-    const uint4 t = *reinterpret_cast<const uint4*>(ptr);
-    c.w[0] = t.x, c.w[1] = t.y, c.w[2] = t.z, c.w[3] = t.w;
-  } else {
-    const uint2 t = *reinterpret_cast<const uint2*>(ptr);
-    c.w[0] = t.x, c.w[1] = t.y;
-  }
-  return c;
-}
-
-template <int BITS>
-__device__ __forceinline__ void store_codes(uint8_t* ptr, const Codes<BITS>& c) {
-  if constexpr (BITS == 8) {
-    *reinterpret_cast<uint4*>(ptr) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
-  } else {
-    *reinterpret_cast<uint2*>(ptr) = make_uint2(c.w[0], c.w[1]);
-  }
-}
-
-template <int BITS>
-__device__ __forceinline__ void unpack(const Codes<BITS>& c, float (&x)[kChunk]) {
+__device__ __forceinline__ void unpack16(const uint32_t* w, float* cu) {
   if constexpr (BITS == 8) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q) {
+      uint32_t x = w[q] ^ 0x80808080u;
+      asm("" : "+v"(x));  // convert bytes in place (v_cvt_f32_ubyte0..3)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) x[4 * q + p] = (float)(int32_t)(int8_t)(c.w[q] >> (8 * p));
-  } else {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-        x[8 * q + p] = (float)(((int32_t)(c.w[q] << (28 - 4 * p))) >> 28);
-  }
-}
-
-template <int BITS>
-__device__ __forceinline__ Codes<BITS> pack(const int32_t (&n)[kChunk]) {
-  Codes<BITS> c;
-  if constexpr (BITS == 8) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      c.w[q] = (uint32_t)(n[4 * q] & 0xFF) | ((uint32_t)(n[4 * q + 1] & 0xFF) << 8) |
-               ((uint32_t)(n[4 * q + 2] & 0xFF) << 16) | ((uint32_t)(n[4 * q + 3] & 0xFF) << 24);
+      for (int p = 0; p < 4; ++p) cu[4 * q + p] = (float)((x >> (8 * p)) & 0xFFu);
+    }
   } else {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      uint32_t w = 0;
+      const uint32_t x = w[q] ^ 0x88888888u;
+      uint32_t lo = x & 0x0F0F0F0Fu;         // even elements, one per byte
+      uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // odd elements
+      asm("" : "+v"(lo));  // convert bytes in place (v_cvt_f32_ubyte0..3)
+      asm("" : "+v"(hi));
 #pragma unroll
-      for (int p = 0; p < 8; ++p) w |= (uint32_t)(n[8 * q + p] & 0xF) << (4 * p);
-      c.w[q] = w;
+      for (int p = 0; p < 4; ++p) {
+        cu[8 * q + 2 * p] = (float)((lo >> (8 * p)) & 0xFFu);
+        cu[8 * q + 2 * p + 1] = (float)((hi >> (8 * p)) & 0xFFu);
+      }
     }
   }
-  return c;
 }
 
-// Requantize one lane's chunk of the updated row S' (value-axis group of the
-// chunk; the group spans lanes_per_group lanes).  Returns the scale s'.
-template <int BITS, bool SR>
-__device__ __forceinline__ float quantize_chunk(const float (&sp)[kChunk], int lanes_per_group,
-                                                uint32_t key, uint32_t block,
-                                                int32_t (&n)[kChunk]) {
-  constexpr float r = (float)((1 << (BITS - 1)) - 1);
-  float m = 0.0f;
+// Bytes [a.BP, b.BP, c.BP, d.BP] of four words.
+template <int BP>
+__device__ __forceinline__ uint32_t gather4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  constexpr uint32_t sel = 0x0C0C0000u | ((4u + BP) << 8) | (uint32_t)BP;
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, sel);
+  return lo | (hi << 16);
+}
+
+// Pack 16 codes (byte BP of each word of src): four words (INT8) or two (INT4).
+template <int BITS, int BP>
+__device__ __forceinline__ void pack16(const uint32_t* src, uint32_t* out) {
+  if constexpr (BITS == 8) {
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j) m = fmaxf(m, fabsf(sp[j]));
-  m = group_max(m, lanes_per_group);
-  float s, inv;
-  group_scale(m, r, s, inv);
-  if constexpr (SR) {
-    float u[kChunk];
-    chunk_uniforms(key, block, u);
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) n[j] = (int32_t)floorf(__builtin_fmaf(sp[j], inv, u[j]));
+    for (int q = 0; q < 4; ++q)
+      out[q] = gather4<BP>(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
   } else {
-    // round-half-even of the exact product: adding 1.5*2^23 inside the fma
-    // leaves rint(sp*inv) in the low mantissa bits (|sp*inv| <= r).
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j)
-      n[j] = __float_as_int(__builtin_fmaf(sp[j], inv, 12582912.0f)) - 0x4B400000;
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t ev = gather4<BP>(src[8 * q], src[8 * q + 2], src[8 * q + 4], src[8 * q + 6]);
+      const uint32_t od = gather4<BP>(src[8 * q + 1], src[8 * q + 3], src[8 * q + 5], src[8 * q + 7]);
+      out[q] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+    }
   }
-  return s;
+}
+
+// floor(x) as int32 in one instruction.
+__device__ __forceinline__ int32_t floor_i32(float x) {
+  int32_t r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Requantize one 16-element chunk with inverse scale inv into 16 packed codes
+// (four words for INT8, two for INT4).  block: the chunk's 16-element block
+// index in the head (stochastic rounding).
+template <int BITS, bool SR>
+__device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t key, uint32_t block,
+                                           uint32_t* out) {
+  uint32_t src[16];
+  if constexpr (SR) {
+    float R[16];
+    block_r16(key, block, R);
+    if (__builtin_expect(inv <= 0x1p100f, 1)) {
+      const float i16 = inv * 65536.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], i16, R[j]));
+    } else {  // groups of tiny magnitude, where inv * 2^16 could overflow
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv, R[j] * (1.0f / 65536.0f))) << 16;
+    }
+    pack16<BITS, 2>(src, out);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv, 12582912.0f));
+    pack16<BITS, 0>(src, out);
+  }
+}
+
+// Requantize the lane's E elements of the updated row S' into 16 bytes of
+// codes.  LPG = 0: two groups per lane (INT4 with G = 16, one per chunk);
+// otherwise one group spanning LPG lanes.  s0/s1: the scales of the lane's
+// groups.
+template <int BITS, bool SR, int E, int LPG>
+__device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t key, uint32_t block0,
+                                               float& s0, float& s1) {
+  constexpr int R = (1 << (BITS - 1)) - 1;
+  float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m0 = fmaxf(m0, fabsf(sp[j]));
+  if constexpr (E == 32) {
+#pragma unroll
+    for (int j = 16; j < 32; ++j) m1 = fmaxf(m1, fabsf(sp[j]));
+  }
+  float inv0, inv1;
+  if constexpr (LPG == 0) {
+    group_scale<R>(m0, s0, inv0);
+    group_scale<R>(m1, s1, inv1);
+  } else {
+    m0 = lanes_max<LPG>(fmaxf(m0, m1));
+    group_scale<R>(m0, s0, inv0);
+    s1 = s0, inv1 = inv0;
+  }
+  uint32_t o[4];
+  quantize16<BITS, SR>(sp, inv0, key, block0, o);
+  if constexpr (E == 32) quantize16<BITS, SR>(sp + 16, inv1, key, block0 + 1, o + 2);
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -234,297 +320,347 @@ __device__ __forceinline__ uint64_t head_code_offset(const KParams& p, int b, in
   return (uint64_t)b * p.bytes_per_b + (uint64_t)(h + n8) * p.head_bytes4;
 }
 
-__device__ __forceinline__ void load16(const float* ptr, float (&x)[kChunk]) {
+template <int N>
+__device__ __forceinline__ void loadv(const float* ptr, float (&x)[N]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < N / 4; ++q) {
     const float4 t = reinterpret_cast<const float4*>(ptr)[q];
     x[4 * q] = t.x, x[4 * q + 1] = t.y, x[4 * q + 2] = t.z, x[4 * q + 3] = t.w;
   }
 }
 
-__device__ __forceinline__ void store16(float* ptr, const float (&x)[kChunk]) {
+template <int N>
+__device__ __forceinline__ void storev(float* ptr, const float (&x)[N]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < N / 4; ++q)
     reinterpret_cast<float4*>(ptr)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
 }
 
-// Per-lane view of one head.
-struct Lane {
-  int b, h, head;  // head = b*H + h
-  int lr;          // chunk index inside the row (lane % LPR)
-  int rsub;        // row offset inside one workgroup iteration
-  int col0;        // first column of the chunk
+// The wave's head and row slice [r0, r1).
+struct Slice {
+  int head, b, h, r0, r1;
 };
+
+__device__ __forceinline__ Slice wave_slice(const KParams& p) {
+  Slice sl;
+  sl.head = blockIdx.x / p.slices;
+  const int part = blockIdx.x - sl.head * p.slices;
+  sl.b = sl.head / p.H;
+  sl.h = sl.head - sl.b * p.H;
+  sl.r0 = part * p.slice_rows;
+  sl.r1 = min(p.dv, sl.r0 + p.slice_rows);
+  return sl;
+}
 
 // ---------------------------------------------------------------------------
 // The decode step on a quantized head of BITS-bit codes.
 // ---------------------------------------------------------------------------
 
-template <int MIXER, bool SR, int LPR, int BITS>
-__device__ __forceinline__ void step_quant_head(const KParams& p, const Lane& L, uint8_t* hcodes,
-                                                float* hscales, const float (&kk)[kChunk],
-                                                const float (&qq)[kChunk], const float (&al)[kChunk],
-                                                float alpha_s, float beta, uint32_t key) {
-  constexpr int DK = LPR * kChunk;
-  constexpr int RPI = (kThreads / 64) * (64 / LPR);
-  constexpr int ROW_BYTES = DK * BITS / 8;
-  constexpr int CHUNK_BYTES = kChunk * BITS / 8;
-  const int lpg = p.G / kChunk;
-  const int ng = DK / p.G;
-  const int n_it = (p.dv + RPI - 1) / RPI;
-  const float* vh = p.v + (size_t)L.head * p.dv;
-  float* oh = p.o ? p.o + (size_t)L.head * p.dv : nullptr;
+struct RowIn {
+  uint4 raw;
+  float s0, s1, v;
+};
 
-  for (int it0 = 0; it0 < n_it; it0 += kBatch) {
-    Codes<BITS> raw[kBatch];
-    float sc[kBatch], vi[kBatch];
-#pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      const int row = (it0 + n) * RPI + L.rsub;
-      if (row < p.dv) {
-        raw[n] = load_codes<BITS>(hcodes + (size_t)row * ROW_BYTES + L.lr * CHUNK_BYTES);
-        sc[n] = hscales[(size_t)row * ng + L.col0 / p.G];
-        vi[n] = vh[row];
-      } else {
-#pragma unroll
-        for (int q = 0; q < BITS / 2; ++q) raw[n].w[q] = 0u;
-        sc[n] = 0.0f;
-        vi[n] = 0.0f;
-      }
+template <int MIXER, bool SR, int DK, int BITS, int G>
+__device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl) {
+  using Gm = Geo<DK, BITS>;
+  constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr float bias = (float)(1 << (BITS - 1));
+  constexpr bool two_groups = G < E;  // INT4 with G = 16
+  constexpr int LPG = two_groups ? 0 : G / E;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = two_groups ? col0 / 16 : col0 / G;  // first group of the lane in its row
+
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const float* vh = p.v + (size_t)sl.head * p.dv;
+  float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
+
+  auto load = [&](int it) {
+    RowIn in;
+    const int row = sl.r0 + it * RPW + rsub;
+    if (it < n_it && row < sl.r1) {
+      in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+      in.s0 = hscales[(size_t)row * ngr + gcol];
+      in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
+      in.v = vh[row];
+    } else {
+      in.raw = make_uint4(0u, 0u, 0u, 0u);
+      in.s0 = in.s1 = in.v = 0.0f;
     }
+    return in;
+  };
+  RowIn ring[kPrefetch];
 #pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      const int row = (it0 + n) * RPI + L.rsub;
-      float c[kChunk], d[kChunk];
-      unpack<BITS>(raw[n], c);
-      // decayed dequantized chunk
+  for (int k = 0; k < kPrefetch; ++k) ring[k] = load(k);
+
+  const uint32_t key = SR ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  float alpha_s = 0.0f, beta = 0.0f;
+  if constexpr (MIXER == kGLA) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+    alpha_s = p.alpha[sl.head];
+    beta = p.beta[sl.head];
+  }
+
+  for (int it0 = 0; it0 < n_it; it0 += kPrefetch) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int it = it0 + k;
+      if (it >= n_it) break;
+      const RowIn in = ring[k];
+      ring[k] = load(it + kPrefetch);
+      const int row = sl.r0 + it * RPW + rsub;
+      const uint32_t w[4] = {in.raw.x, in.raw.y, in.raw.z, in.raw.w};
+      float d[E];
+      unpack16<BITS>(w, d);
+      if constexpr (E == 32) unpack16<BITS>(w + 2, d + 16);
+      // decayed dequantized values (exactly the rounded c*(s*alpha) / (c*s)*alpha_j)
       if constexpr (MIXER == kGLA) {
+        const float nb0 = -bias * in.s0, nb1 = -bias * in.s1;
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) d[j] = (c[j] * sc[n]) * al[j];
+        for (int j = 0; j < E; ++j)
+          d[j] = __builtin_fmaf(d[j], j < 16 ? in.s0 : in.s1, j < 16 ? nb0 : nb1) * al[j];
       } else {
-        const float sa = sc[n] * alpha_s;
+        const float sa0 = in.s0 * alpha_s, sa1 = in.s1 * alpha_s;
+        const float nb0 = -bias * sa0, nb1 = -bias * sa1;
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) d[j] = c[j] * sa;
+        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], j < 16 ? sa0 : sa1, j < 16 ? nb0 : nb1);
       }
       // write weight
-      float w;
+      float wt;
       if constexpr (MIXER == kGDN) {
-        const float u = row_sum<LPR>(chunk_dot(d, kk));
-        w = beta * (vi[n] - u);
+        const float u = row_sum<LPR>(lane_dot(d, kk));
+        wt = beta * (in.v - u);
       } else if constexpr (MIXER == kGLA) {
-        w = vi[n];
+        wt = in.v;
       } else {
-        w = beta * vi[n];
+        wt = beta * in.v;
       }
-      // rank-1 write and readout from the full-precision S'
-      float sp[kChunk];
+      // rank-1 write (in place) and readout from the full-precision S'
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) sp[j] = __builtin_fmaf(w, kk[j], d[j]);
-      const float o = row_sum<LPR>(chunk_dot(sp, qq));
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      const float o = row_sum<LPR>(lane_dot(d, qq));
       // requantize
-      int32_t code[kChunk];
-      const uint32_t block = (uint32_t)row * LPR + (uint32_t)L.lr;
-      const float s_new = quantize_chunk<BITS, SR>(sp, lpg, key, block, code);
-      if (row < p.dv) {
-        store_codes<BITS>(hcodes + (size_t)row * ROW_BYTES + L.lr * CHUNK_BYTES, pack<BITS>(code));
-        if (L.lr % lpg == 0) hscales[(size_t)row * ng + L.col0 / p.G] = s_new;
-        if (oh && L.lr == 0) oh[row] = o;
+      float s0, s1;
+      const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
+      const uint4 packed = quantize_lane<BITS, SR, E, LPG>(d, key, block0, s0, s1);
+      if (row < sl.r1) {
+        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        if constexpr (two_groups) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+          hscales[(size_t)row * ngr + gcol + 1] = s1;
+        } else if (lr % LPG == 0) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+        }
+        if (oh && lr == 0) oh[row] = o;
       }
     }
   }
 }
 
-// The same step on an unquantized FP32 head.
-template <int MIXER, int LPR>
-__device__ __forceinline__ void step_fp32_head(const KParams& p, const Lane& L, float* hS,
-                                               const float (&kk)[kChunk], const float (&qq)[kChunk],
-                                               const float (&al)[kChunk], float alpha_s, float beta) {
-  constexpr int DK = LPR * kChunk;
-  constexpr int RPI = (kThreads / 64) * (64 / LPR);
-  const int n_it = (p.dv + RPI - 1) / RPI;
-  const float* vh = p.v + (size_t)L.head * p.dv;
-  float* oh = p.o ? p.o + (size_t)L.head * p.dv : nullptr;
-  for (int it0 = 0; it0 < n_it; it0 += kBatch) {
-    float x[kBatch][kChunk], vi[kBatch];
+// The same step on an unquantized FP32 head: 16 elements per lane.
+template <int MIXER, int DK>
+__device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl) {
+  constexpr int E = 16, LPR = DK / E, RPW = 64 / LPR;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  float* hS = reinterpret_cast<float*>(p.state) + (size_t)sl.head * p.dv * DK;
+  const float* vh = p.v + (size_t)sl.head * p.dv;
+  float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
+  struct FIn {
+    float x[E];
+    float v;
+  };
+  auto load = [&](int it) {
+    FIn in;
+    const int row = sl.r0 + it * RPW + rsub;
+    if (it < n_it && row < sl.r1) {
+      loadv(hS + (size_t)row * DK + col0, in.x);
+      in.v = vh[row];
+    } else {
 #pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      const int row = (it0 + n) * RPI + L.rsub;
-      if (row < p.dv) {
-        load16(hS + (size_t)row * DK + L.col0, x[n]);
-        vi[n] = vh[row];
-      } else {
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) x[n][j] = 0.0f;
-        vi[n] = 0.0f;
-      }
+      for (int j = 0; j < E; ++j) in.x[j] = 0.0f;
+      in.v = 0.0f;
     }
+    return in;
+  };
+  FIn ring[kPrefetch];
 #pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      const int row = (it0 + n) * RPI + L.rsub;
-      float d[kChunk];
+  for (int k = 0; k < kPrefetch; ++k) ring[k] = load(k);
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  float alpha_s = 0.0f, beta = 0.0f;
+  if constexpr (MIXER == kGLA) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) d[j] = x[n][j] * (MIXER == kGLA ? al[j] : alpha_s);
-      float w;
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+    alpha_s = p.alpha[sl.head];
+    beta = p.beta[sl.head];
+  }
+  for (int it0 = 0; it0 < n_it; it0 += kPrefetch) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int it = it0 + k;
+      if (it >= n_it) break;
+      const FIn in = ring[k];
+      ring[k] = load(it + kPrefetch);
+      const int row = sl.r0 + it * RPW + rsub;
+      float d[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = in.x[j] * (MIXER == kGLA ? al[j] : alpha_s);
+      float wt;
       if constexpr (MIXER == kGDN) {
-        const float u = row_sum<LPR>(chunk_dot(d, kk));
-        w = beta * (vi[n] - u);
+        const float u = row_sum<LPR>(lane_dot(d, kk));
+        wt = beta * (in.v - u);
       } else if constexpr (MIXER == kGLA) {
-        w = vi[n];
+        wt = in.v;
       } else {
-        w = beta * vi[n];
+        wt = beta * in.v;
       }
-      float sp[kChunk];
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) sp[j] = __builtin_fmaf(w, kk[j], d[j]);
-      const float o = row_sum<LPR>(chunk_dot(sp, qq));
-      if (row < p.dv) {
-        store16(hS + (size_t)row * DK + L.col0, sp);
-        if (oh && L.lr == 0) oh[row] = o;
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      const float o = row_sum<LPR>(lane_dot(d, qq));
+      if (row < sl.r1) {
+        storev(hS + (size_t)row * DK + col0, d);
+        if (oh && lr == 0) oh[row] = o;
       }
     }
   }
 }
 
 // Import (quantize an FP32 state), export (dequantize) and readout of a
-// quantized head.
-template <int OP, bool SR, int LPR, int BITS>
-__device__ __forceinline__ void aux_quant_head(const KParams& p, const Lane& L, uint8_t* hcodes,
-                                               float* hscales, const float (&qq)[kChunk],
-                                               uint32_t key) {
-  constexpr int DK = LPR * kChunk;
-  constexpr int RPI = (kThreads / 64) * (64 / LPR);
-  constexpr int ROW_BYTES = DK * BITS / 8;
-  constexpr int CHUNK_BYTES = kChunk * BITS / 8;
-  const int lpg = p.G / kChunk;
-  const int ng = DK / p.G;
-  const size_t hoff = (size_t)L.head * p.dv * DK;
-  for (int it = 0; it * RPI < p.dv; ++it) {
-    const int row = it * RPI + L.rsub;
-    const bool ok = row < p.dv;
+// quantized head, with the step's lane geometry and quantizer.
+template <int OP, bool SR, int DK, int BITS, int G>
+__device__ __forceinline__ void aux_quant_head(const KParams& p, const Slice sl) {
+  using Gm = Geo<DK, BITS>;
+  constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr float bias = (float)(1 << (BITS - 1));
+  constexpr bool two_groups = G < E;
+  constexpr int LPG = two_groups ? 0 : G / E;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = two_groups ? col0 / 16 : col0 / G;
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const size_t hoff = (size_t)sl.head * p.dv * DK;
+  const uint32_t key = (OP == kImport && SR) ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float qq[E];
+  if constexpr (OP == kReadout) loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  for (int rbase = sl.r0; rbase < sl.r1; rbase += RPW) {
+    const int row = rbase + rsub;
+    const bool ok = row < sl.r1;
     if constexpr (OP == kImport) {
-      float x[kChunk];
+      float x[E];
       if (ok)
-        load16(p.src + hoff + (size_t)row * DK + L.col0, x);
+        loadv(p.src + hoff + (size_t)row * DK + col0, x);
       else
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) x[j] = 0.0f;
-      int32_t code[kChunk];
-      const uint32_t block = (uint32_t)row * LPR + (uint32_t)L.lr;
-      const float s_new = quantize_chunk<BITS, SR>(x, lpg, key, block, code);
+        for (int j = 0; j < E; ++j) x[j] = 0.0f;
+      float s0, s1;
+      const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
+      const uint4 packed = quantize_lane<BITS, SR, E, LPG>(x, key, block0, s0, s1);
       if (ok) {
-        store_codes<BITS>(hcodes + (size_t)row * ROW_BYTES + L.lr * CHUNK_BYTES, pack<BITS>(code));
-        if (L.lr % lpg == 0) hscales[(size_t)row * ng + L.col0 / p.G] = s_new;
+        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        if constexpr (two_groups) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+          hscales[(size_t)row * ngr + gcol + 1] = s1;
+        } else if (lr % LPG == 0) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+        }
       }
     } else {
-      Codes<BITS> raw;
-      float s = 0.0f;
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      float s0 = 0.0f, s1 = 0.0f;
       if (ok) {
-        raw = load_codes<BITS>(hcodes + (size_t)row * ROW_BYTES + L.lr * CHUNK_BYTES);
-        s = hscales[(size_t)row * ng + L.col0 / p.G];
-      } else {
-#pragma unroll
-        for (int q = 0; q < BITS / 2; ++q) raw.w[q] = 0u;
+        raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+        s0 = hscales[(size_t)row * ngr + gcol];
+        s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : s0;
       }
-      float c[kChunk], x[kChunk];
-      unpack<BITS>(raw, c);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float x[E];
+      unpack16<BITS>(w, x);
+      if constexpr (E == 32) unpack16<BITS>(w + 2, x + 16);
+      const float nb0 = -bias * s0, nb1 = -bias * s1;
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) x[j] = c[j] * s;
+      for (int j = 0; j < E; ++j) x[j] = __builtin_fmaf(x[j], j < 16 ? s0 : s1, j < 16 ? nb0 : nb1);
       if constexpr (OP == kExport) {
-        if (ok) store16(p.dst + hoff + (size_t)row * DK + L.col0, x);
+        if (ok) storev(p.dst + hoff + (size_t)row * DK + col0, x);
       } else {
-        const float o = row_sum<LPR>(chunk_dot(x, qq));
-        if (ok && L.lr == 0) p.o[(size_t)L.head * p.dv + row] = o;
+        const float o = row_sum<LPR>(lane_dot(x, qq));
+        if (ok && lr == 0) p.o[(size_t)sl.head * p.dv + row] = o;
       }
     }
   }
-}
-
-template <int LPR>
-__device__ __forceinline__ Lane make_lane(const KParams& p) {
-  Lane L;
-  L.head = blockIdx.x;
-  L.b = L.head / p.H;
-  L.h = L.head - L.b * p.H;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  L.lr = lane % LPR;
-  L.rsub = wave * (64 / LPR) + lane / LPR;
-  L.col0 = L.lr * kChunk;
-  return L;
 }
 
 // ---------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------
 
-template <int MIXER, bool SR, bool FP32, int LPR>
+template <int MIXER, bool SR, int DK, int G>
 __global__ __launch_bounds__(kThreads) void step_kernel(const KParams p) {
-  constexpr int DK = LPR * kChunk;
-  const Lane L = make_lane<LPR>(p);
-  float kk[kChunk], qq[kChunk], al[kChunk];
-  load16(p.k + (size_t)L.head * DK + L.col0, kk);
-  load16(p.q + (size_t)L.head * DK + L.col0, qq);
-  float alpha_s = 0.0f, beta = 0.0f;
-  if constexpr (MIXER == kGLA) {
-    load16(p.alpha + (size_t)L.head * DK + L.col0, al);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) al[j] = 0.0f;
-    alpha_s = p.alpha[L.head];
-    beta = p.beta[L.head];
-  }
-  if constexpr (FP32) {
-    float* hS = reinterpret_cast<float*>(p.state) + (size_t)L.head * p.dv * DK;
-    step_fp32_head<MIXER, LPR>(p, L, hS, kk, qq, al, alpha_s, beta);
-  } else {
-    uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, L.b, L.h);
-    float* hscales = p.scales + (size_t)L.head * p.dv * (DK / p.G);
-    const uint32_t key = SR ? head_key(p, (uint32_t)L.b, (uint32_t)L.h) : 0u;
-    if (head_is_int8(p, L.h))
-      step_quant_head<MIXER, SR, LPR, 8>(p, L, hcodes, hscales, kk, qq, al, alpha_s, beta, key);
-    else
-      step_quant_head<MIXER, SR, LPR, 4>(p, L, hcodes, hscales, kk, qq, al, alpha_s, beta, key);
-  }
+  const Slice sl = wave_slice(p);
+  if (head_is_int8(p, sl.h))
+    step_quant_head<MIXER, SR, DK, 8, G>(p, sl);
+  else
+    step_quant_head<MIXER, SR, DK, 4, G>(p, sl);
 }
 
-template <int OP, bool SR, int LPR>
+template <int MIXER, int DK>
+__global__ __launch_bounds__(kThreads) void step_fp32_kernel(const KParams p) {
+  step_fp32_head<MIXER, DK>(p, wave_slice(p));
+}
+
+template <int OP, bool SR, int DK, int G>
 __global__ __launch_bounds__(kThreads) void aux_kernel(const KParams p) {
-  constexpr int DK = LPR * kChunk;
-  const Lane L = make_lane<LPR>(p);
-  float qq[kChunk];
-  if constexpr (OP == kReadout)
-    load16(p.q + (size_t)L.head * DK + L.col0, qq);
+  const Slice sl = wave_slice(p);
+  if (head_is_int8(p, sl.h))
+    aux_quant_head<OP, SR, DK, 8, G>(p, sl);
   else
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) qq[j] = 0.0f;
-  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, L.b, L.h);
-  float* hscales = p.scales + (size_t)L.head * p.dv * (DK / p.G);
-  const uint32_t key = (OP == kImport && SR) ? head_key(p, (uint32_t)L.b, (uint32_t)L.h) : 0u;
-  if (head_is_int8(p, L.h))
-    aux_quant_head<OP, SR, LPR, 8>(p, L, hcodes, hscales, qq, key);
-  else
-    aux_quant_head<OP, SR, LPR, 4>(p, L, hcodes, hscales, qq, key);
+    aux_quant_head<OP, SR, DK, 4, G>(p, sl);
 }
 
 // FP32-state readout: o = S q.
-template <int LPR>
+template <int DK>
 __global__ __launch_bounds__(kThreads) void readout_fp32_kernel(const KParams p) {
-  constexpr int DK = LPR * kChunk;
-  constexpr int RPI = (kThreads / 64) * (64 / LPR);
-  const Lane L = make_lane<LPR>(p);
-  float qq[kChunk];
-  load16(p.q + (size_t)L.head * DK + L.col0, qq);
-  const float* hS = reinterpret_cast<const float*>(p.state) + (size_t)L.head * p.dv * DK;
-  for (int it = 0; it * RPI < p.dv; ++it) {
-    const int row = it * RPI + L.rsub;
-    float x[kChunk];
-    if (row < p.dv)
-      load16(hS + (size_t)row * DK + L.col0, x);
+  constexpr int E = 16, LPR = DK / E, RPW = 64 / LPR;
+  const Slice sl = wave_slice(p);
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  float qq[E];
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  const float* hS = reinterpret_cast<const float*>(p.state) + (size_t)sl.head * p.dv * DK;
+  for (int rbase = sl.r0; rbase < sl.r1; rbase += RPW) {
+    const int row = rbase + rsub;
+    float x[E];
+    if (row < sl.r1)
+      loadv(hS + (size_t)row * DK + col0, x);
     else
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) x[j] = 0.0f;
-    const float o = row_sum<LPR>(chunk_dot(x, qq));
-    if (row < p.dv && L.lr == 0) p.o[(size_t)L.head * p.dv + row] = o;
+      for (int j = 0; j < E; ++j) x[j] = 0.0f;
+    const float o = row_sum<LPR>(lane_dot(x, qq));
+    if (row < sl.r1 && lr == 0) p.o[(size_t)sl.head * p.dv + row] = o;
   }
 }
 
@@ -532,38 +668,65 @@ __global__ __launch_bounds__(kThreads) void readout_fp32_kernel(const KParams p)
 // Dispatch.
 // ---------------------------------------------------------------------------
 
-template <int LPR>
-hipError_t launch_lpr(Op op, int mixer, int sr, int fp32, const KParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.H)), block(kThreads);
+inline dim3 grid_of(const KParams& p) { return dim3((unsigned)(p.B * p.H * p.slices)); }
+
+template <int DK, int G>
+hipError_t launch_quant(Op op, int mixer, int sr, const KParams& p, hipStream_t s) {
+  const dim3 grid = grid_of(p), block(kThreads);
   if (op == kStep) {
-#define QS_STEP(M, S, F) \
-  if (mixer == M && sr == S && fp32 == F) { step_kernel<M, S, F, LPR><<<grid, block, 0, s>>>(p); return hipGetLastError(); }
-    QS_STEP(kGDN, false, false) QS_STEP(kGDN, true, false) QS_STEP(kGLA, false, false)
-    QS_STEP(kGLA, true, false) QS_STEP(kScalar, false, false) QS_STEP(kScalar, true, false)
-    QS_STEP(kGDN, false, true) QS_STEP(kGLA, false, true) QS_STEP(kScalar, false, true)
+#define QS_STEP(M, S)                                           \
+  if (mixer == M && sr == S) {                                  \
+    step_kernel<M, S, DK, G><<<grid, block, 0, s>>>(p);         \
+    return hipGetLastError();                                   \
+  }
+    QS_STEP(kGDN, false) QS_STEP(kGDN, true) QS_STEP(kGLA, false)
+    QS_STEP(kGLA, true) QS_STEP(kScalar, false) QS_STEP(kScalar, true)
 #undef QS_STEP
     return hipErrorInvalidValue;
   }
+  switch (op) {
+    case kImport:
+      if (sr)
+        aux_kernel<kImport, true, DK, G><<<grid, block, 0, s>>>(p);
+      else
+        aux_kernel<kImport, false, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    case kExport:
+      aux_kernel<kExport, false, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    case kReadout:
+      aux_kernel<kReadout, false, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <int DK>
+hipError_t launch_dk(Op op, int mixer, int sr, int fp32, const KParams& p, hipStream_t s) {
+  const dim3 grid = grid_of(p), block(kThreads);
   if (fp32) {
+    if (op == kStep) {
+      switch (mixer) {
+        case kGDN: step_fp32_kernel<kGDN, DK><<<grid, block, 0, s>>>(p); break;
+        case kGLA: step_fp32_kernel<kGLA, DK><<<grid, block, 0, s>>>(p); break;
+        case kScalar: step_fp32_kernel<kScalar, DK><<<grid, block, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
     if (op == kReadout) {
-      readout_fp32_kernel<LPR><<<grid, block, 0, s>>>(p);
+      readout_fp32_kernel<DK><<<grid, block, 0, s>>>(p);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;  // import/export of an FP32 state are plain copies
   }
-  switch (op) {
-    case kImport:
-      if (sr) aux_kernel<kImport, true, LPR><<<grid, block, 0, s>>>(p);
-      else aux_kernel<kImport, false, LPR><<<grid, block, 0, s>>>(p);
-      return hipGetLastError();
-    case kExport:
-      aux_kernel<kExport, false, LPR><<<grid, block, 0, s>>>(p);
-      return hipGetLastError();
-    case kReadout:
-      aux_kernel<kReadout, false, LPR><<<grid, block, 0, s>>>(p);
-      return hipGetLastError();
-    default:
-      return hipErrorInvalidValue;
+  switch (p.G) {
+    case 16: return launch_quant<DK, 16>(op, mixer, sr, p, s);
+    case 32: return launch_quant<DK, 32>(op, mixer, sr, p, s);
+    case 64: return launch_quant<DK, 64>(op, mixer, sr, p, s);
+    case 128: return launch_quant<DK, 128>(op, mixer, sr, p, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -571,12 +734,15 @@ hipError_t launch_lpr(Op op, int mixer, int sr, int fp32, const KParams& p, hipS
 
 hipError_t launch(Op op, int mixer, int rounding, int fp32, int dk, const KParams& p,
                   hipStream_t stream) {
+  if (p.slices < 1 || p.slice_rows < 1 || p.slice_rows % 32 != 0 ||
+      (int64_t)p.slices * p.slice_rows < p.dv)
+    return hipErrorInvalidValue;
   const int sr = (rounding == 1 && !fp32) ? 1 : 0;
   const int f = fp32 ? 1 : 0;
   switch (dk) {
-    case 64: return launch_lpr<4>(op, mixer, sr, f, p, stream);
-    case 128: return launch_lpr<8>(op, mixer, sr, f, p, stream);
-    case 256: return launch_lpr<16>(op, mixer, sr, f, p, stream);
+    case 64: return launch_dk<64>(op, mixer, sr, f, p, stream);
+    case 128: return launch_dk<128>(op, mixer, sr, f, p, stream);
+    case 256: return launch_dk<256>(op, mixer, sr, f, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

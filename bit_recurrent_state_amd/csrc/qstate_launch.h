@@ -21,6 +21,8 @@ struct KParams {
   const float* src;      // import: FP32 state to quantize
   float* dst;            // export: dequantized FP32 state
   int32_t B, H, dv, G;
+  int32_t slices;        // waves per head (row slices); the grid is B*H*slices
+  int32_t slice_rows;    // rows per slice, a multiple of 32
   uint64_t bytes_per_b;  // code bytes of one batch row (all heads)
   uint32_t head_bytes4;  // code bytes of an INT4 head = dv*dk/2
   uint32_t int8_mask[8]; // bit h set: head h stores INT8 codes

@@ -1,0 +1,99 @@
+"""CPU checks of the floating-point identities the gfx950 kernels rely on to
+compute the documented semantics with fewer instructions.  Each identity is
+exact IEEE-754 binary32 arithmetic, so a C program with correctly rounded
+fmaf (no contraction) checks it exhaustively or on large random samples:
+
+1. s = m / r for r in {7, 127}: with c = RN(1/r), q = m*c, e = fma(-q, r, m),
+   fma(e, c, q) == RN(m / r) for every float mantissa (three exponent ranges).
+2. Offset-binary dequantization: fma(c + 2^(b-1), sa, -2^(b-1)*sa) == RN(c*sa)
+   for every code c and random (incl. subnormal) sa below 2^120, the library's
+   supported state magnitude (beyond it 2^(b-1)*sa itself may overflow).
+3. Stochastic rounding via an exact 2^16 scaling:
+   floor(fma(x, inv*2^16, R)) >> 16 == floor(fma(x, inv, R*2^-16)).
+4. Round-to-nearest via the 1.5*2^23 constant: the low bits of
+   fma(x, inv, 1.5*2^23) hold rint(x*inv) of the exact product when |x*inv| <= r.
+"""
+
+import os
+import subprocess
+import tempfile
+
+SRC = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+static float f_of(uint32_t u){float f; memcpy(&f,&u,4); return f;}
+static uint32_t u_of(float f){uint32_t u; memcpy(&u,&f,4); return u;}
+static uint64_t s = 88172645463325252ull;
+static uint32_t rnd(void){ s ^= s << 13; s ^= s >> 7; s ^= s << 17; return (uint32_t)(s >> 11); }
+/* largest float v with v*m <= r */
+static float inv_rz(float m, float r){ float v = (float)((double)r / (double)m);
+  while ((double)v * (double)m > (double)r) v = nextafterf(v, 0.0f); return v; }
+int main(void){
+  long bad = 0;
+  /* 1 */
+  const float rs[2] = {7.0f, 127.0f};
+  for (int t = 0; t < 2; ++t) {
+    const float r = rs[t], c = 1.0f / r;
+    for (uint32_t mant = 0; mant < (1u << 23); ++mant)
+      for (int ex = 0; ex < 3; ++ex) {
+        const uint32_t e8 = ex == 0 ? 127 : (ex == 1 ? 28 : 200);
+        const float m = f_of((e8 << 23) | mant);
+        const float q = m * c;
+        const float got = fmaf(fmaf(-q, r, m), c, q);
+        if (got != m / r) { if (bad < 5) printf("div r=%g m=%a\n", r, m); ++bad; }
+      }
+  }
+  printf("identity1 %ld\n", bad);
+  /* 2 */
+  long bad2 = 0;
+  for (int bits = 4; bits <= 8; bits += 4) {
+    const int r = (1 << (bits - 1)) - 1; const float bias = (float)(1 << (bits - 1));
+    for (int it = 0; it < 200000; ++it) {
+      uint32_t u = rnd() & 0x7fffffffu;
+      if ((u >> 23) >= 247) u &= 0x3fffffffu;  /* supported range: |sa| < 2^120 */
+      const float sa = f_of(u);
+      for (int c = -r; c <= r; ++c) {
+        const float got = fmaf((float)(c + (1 << (bits - 1))), sa, -bias * sa);
+        const float want = (float)c * sa;
+        if (u_of(got) != u_of(want) && !(got == 0.0f && want == 0.0f)) { if (bad2 < 5) printf("deq c=%d sa=%a\n", c, sa); ++bad2; }
+      }
+    }
+  }
+  printf("identity2 %ld\n", bad2);
+  /* 3 and 4 */
+  long bad3 = 0, bad4 = 0;
+  for (int bits = 4; bits <= 8; bits += 4) {
+    const float r = (float)((1 << (bits - 1)) - 1);
+    for (int it = 0; it < 3000000; ++it) {
+      const float m = f_of(((uint32_t)(97 + rnd() % 60) << 23) | (rnd() & 0x7fffffu));
+      const float inv = inv_rz(m, r);
+      const float x = (rnd() & 1 ? -1.0f : 1.0f) * m * (float)(rnd() & 0xffffff) / 16777216.0f;
+      const uint32_t R = rnd() & 0xffffu;
+      const int a = ((int)floorf(fmaf(x, inv * 65536.0f, (float)R))) >> 16;
+      const int b = (int)floorf(fmaf(x, inv, (float)R * (1.0f / 65536.0f)));
+      if (a != b) { if (bad3 < 5) printf("sr x=%a inv=%a R=%u\n", x, inv, R); ++bad3; }
+      const int n = (int)(u_of(fmaf(x, inv, 12582912.0f)) - 0x4B400000u);
+      const int w = (int)rint((double)x * (double)inv);
+      if (n != w || abs(w) > (int)r) { if (bad4 < 5) printf("rtn x=%a inv=%a\n", x, inv); ++bad4; }
+    }
+  }
+  printf("identity3 %ld\nidentity4 %ld\n", bad3, bad4);
+  return (bad || bad2 || bad3 || bad4) ? 1 : 0;
+}
+"""
+
+
+def test_kernel_float_identities():
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "ident.c")
+        exe = os.path.join(d, "ident")
+        open(c, "w").write(SRC)
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-o", exe, c, "-lm"],
+                       check=True)
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+        lines = dict(l.split() for l in r.stdout.splitlines() if l.startswith("identity"))
+        assert r.returncode == 0, r.stdout
+        assert lines == {"identity1": "0", "identity2": "0", "identity3": "0", "identity4": "0"}
