@@ -381,24 +381,7 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
   float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
   const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
 
-  auto load = [&](int it) {
-    RowIn in;
-    const int row = sl.r0 + it * RPW + rsub;
-    if (it < n_it && row < sl.r1) {
-      in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
-      in.s0 = hscales[(size_t)row * ngr + gcol];
-      in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
-      in.v = vh[row];
-    } else {
-      in.raw = make_uint4(0u, 0u, 0u, 0u);
-      in.s0 = in.s1 = in.v = 0.0f;
-    }
-    return in;
-  };
-  RowIn ring[kPrefetch];
-#pragma unroll
-  for (int k = 0; k < kPrefetch; ++k) ring[k] = load(k);
-
+  // per-head vectors first, so that waiting for them never drains the ring
   const uint32_t key = SR ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
   float kk[E], qq[E], al[E];
   loadv(p.k + (size_t)sl.head * DK + col0, kk);
@@ -412,27 +395,52 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
     alpha_s = p.alpha[sl.head];
     beta = p.beta[sl.head];
   }
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
 
-  for (int it0 = 0; it0 < n_it; it0 += kPrefetch) {
+  // Every lane always loads an in-range row: rows past the slice (the last
+  // iteration's tail and the prefetches beyond the end) re-read the slice's
+  // last row and are never stored.  Branch-free loads keep the ring's loads
+  // in flight across iterations.
+  auto load = [&](int it) {
+    RowIn in;
+    const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
+    in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+    in.s0 = hscales[(size_t)row * ngr + gcol];
+    in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
+    in.v = vh[row];
+    return in;
+  };
+  RowIn ring[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    ring[k] = load(k);
+    asm volatile("" ::: "memory");  // issue the slots in order: slot 0 is needed first
+  }
+
+  // Trips of kPrefetch iterations.  A slot's next load is issued once its
+  // previous contents (codes, scales, v) are dead, so the load lands in the
+  // same registers and stays in flight across trips.
+  // Iterations past the end compute on clamped rows and store nothing.
+  const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
+  for (int t = 0; t < n_trips; ++t) {
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
-      const int it = it0 + k;
-      if (it >= n_it) break;
-      const RowIn in = ring[k];
-      ring[k] = load(it + kPrefetch);
+      const int it = t * kPrefetch + k;
       const int row = sl.r0 + it * RPW + rsub;
-      const uint32_t w[4] = {in.raw.x, in.raw.y, in.raw.z, in.raw.w};
+      const bool store_ok = it < n_it && row < sl.r1;
+      const uint32_t w[4] = {ring[k].raw.x, ring[k].raw.y, ring[k].raw.z, ring[k].raw.w};
+      const float s_0 = ring[k].s0, s_1 = ring[k].s1, vrow = ring[k].v;
       float d[E];
       unpack16<BITS>(w, d);
       if constexpr (E == 32) unpack16<BITS>(w + 2, d + 16);
       // decayed dequantized values (exactly the rounded c*(s*alpha) / (c*s)*alpha_j)
       if constexpr (MIXER == kGLA) {
-        const float nb0 = -bias * in.s0, nb1 = -bias * in.s1;
+        const float nb0 = -bias * s_0, nb1 = -bias * s_1;
 #pragma unroll
         for (int j = 0; j < E; ++j)
-          d[j] = __builtin_fmaf(d[j], j < 16 ? in.s0 : in.s1, j < 16 ? nb0 : nb1) * al[j];
+          d[j] = __builtin_fmaf(d[j], j < 16 ? s_0 : s_1, j < 16 ? nb0 : nb1) * al[j];
       } else {
-        const float sa0 = in.s0 * alpha_s, sa1 = in.s1 * alpha_s;
+        const float sa0 = s_0 * alpha_s, sa1 = s_1 * alpha_s;
         const float nb0 = -bias * sa0, nb1 = -bias * sa1;
 #pragma unroll
         for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], j < 16 ? sa0 : sa1, j < 16 ? nb0 : nb1);
@@ -441,21 +449,22 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
       float wt;
       if constexpr (MIXER == kGDN) {
         const float u = row_sum<LPR>(lane_dot(d, kk));
-        wt = beta * (in.v - u);
+        wt = beta * (vrow - u);
       } else if constexpr (MIXER == kGLA) {
-        wt = in.v;
+        wt = vrow;
       } else {
-        wt = beta * in.v;
+        wt = beta * vrow;
       }
       // rank-1 write (in place) and readout from the full-precision S'
 #pragma unroll
       for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
       const float o = row_sum<LPR>(lane_dot(d, qq));
       // requantize
       float s0, s1;
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
       const uint4 packed = quantize_lane<BITS, SR, E, LPG>(d, key, block0, s0, s1);
-      if (row < sl.r1) {
+      if (store_ok) {
         *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
         if constexpr (two_groups) {
           hscales[(size_t)row * ngr + gcol] = s0;
@@ -485,22 +494,6 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
     float x[E];
     float v;
   };
-  auto load = [&](int it) {
-    FIn in;
-    const int row = sl.r0 + it * RPW + rsub;
-    if (it < n_it && row < sl.r1) {
-      loadv(hS + (size_t)row * DK + col0, in.x);
-      in.v = vh[row];
-    } else {
-#pragma unroll
-      for (int j = 0; j < E; ++j) in.x[j] = 0.0f;
-      in.v = 0.0f;
-    }
-    return in;
-  };
-  FIn ring[kPrefetch];
-#pragma unroll
-  for (int k = 0; k < kPrefetch; ++k) ring[k] = load(k);
   float kk[E], qq[E], al[E];
   loadv(p.k + (size_t)sl.head * DK + col0, kk);
   loadv(p.q + (size_t)sl.head * DK + col0, qq);
@@ -513,30 +506,46 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
     alpha_s = p.alpha[sl.head];
     beta = p.beta[sl.head];
   }
-  for (int it0 = 0; it0 < n_it; it0 += kPrefetch) {
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
+  // branch-free loads of in-range rows (see step_quant_head)
+  auto load = [&](int it) {
+    FIn in;
+    const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
+    loadv(hS + (size_t)row * DK + col0, in.x);
+    in.v = vh[row];
+    return in;
+  };
+  FIn ring[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    ring[k] = load(k);
+    asm volatile("" ::: "memory");  // issue the slots in order: slot 0 is needed first
+  }
+  const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
+  for (int t = 0; t < n_trips; ++t) {
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
-      const int it = it0 + k;
-      if (it >= n_it) break;
-      const FIn in = ring[k];
-      ring[k] = load(it + kPrefetch);
+      const int it = t * kPrefetch + k;
       const int row = sl.r0 + it * RPW + rsub;
+      const bool store_ok = it < n_it && row < sl.r1;
+      const float vrow = ring[k].v;
       float d[E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) d[j] = in.x[j] * (MIXER == kGLA ? al[j] : alpha_s);
+      for (int j = 0; j < E; ++j) d[j] = ring[k].x[j] * (MIXER == kGLA ? al[j] : alpha_s);
       float wt;
       if constexpr (MIXER == kGDN) {
         const float u = row_sum<LPR>(lane_dot(d, kk));
-        wt = beta * (in.v - u);
+        wt = beta * (vrow - u);
       } else if constexpr (MIXER == kGLA) {
-        wt = in.v;
+        wt = vrow;
       } else {
-        wt = beta * in.v;
+        wt = beta * vrow;
       }
 #pragma unroll
       for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
       const float o = row_sum<LPR>(lane_dot(d, qq));
-      if (row < sl.r1) {
+      if (store_ok) {
         storev(hS + (size_t)row * DK + col0, d);
         if (oh && lr == 0) oh[row] = o;
       }
