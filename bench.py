@@ -32,6 +32,28 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized-state decode steps/s and HBM GB/s (% of peak) at B=256, INT8/INT4"
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", "qstate_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts (scaled by the same counters on a copy of known size); None when the
+    kernel source changed since they were taken."""
+    try:
+        import json as _j
+        t = _j.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(workload_name)
+    if not e or t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return e["hbm_bytes_per_launch"]
 
 
 def algorithmic_bytes(w, hb) -> int:
@@ -188,8 +210,8 @@ def main():
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": nbytes},
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name),
+                     "algorithmic_bytes_per_launch": nbytes},
     }
 
     if not args.no_extras:
@@ -230,7 +252,21 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         result["copy_ceiling_gbps"] = 2 * 4 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del a, bb
+        del bb
+        # plain in-place read-modify-write of the same size (the state update's access pattern)
+        ai = a.view(torch.int32)
+        for _ in range(3):
+            ai.bitwise_xor_(0x5A5A5A5A)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            ai.bitwise_xor_(0x5A5A5A5A)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        result["rmw_ceiling_gbps"] = 2 * 4 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        result["hbm_frac_of_rmw_ceiling"] = gbps / result["rmw_ceiling_gbps"]
+        del a, ai
+        torch.cuda.empty_cache()
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, hb, args.cpu_seconds)
