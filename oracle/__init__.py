@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.cpp")
 LIB = os.path.join(HERE, "liboracle.so")
 
-GDN, GLA, SCALAR = 0, 1, 2
+GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR = 0, 1
 
 
@@ -191,7 +191,7 @@ def head_step(c: Cfg, b, h, bits, codes, scales, q, k, v, alpha, beta, step,
     assert scales.size == c.dv * (c.dk // c.G)
     q, k, v, alpha = _f32(q), _f32(k), _f32(v), _f32(alpha)
     assert q.size == c.dk and k.size == c.dk and v.size == c.dv
-    assert alpha.size == (c.dk if c.mixer == GLA else 1)
+    assert alpha.size == (c.dk if c.mixer in (GLA, KDA) else 1)
     o = np.zeros(c.dv, np.float32)
     pre = np.zeros((c.dv, c.dk), np.float32) if want_pre else None
     xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None

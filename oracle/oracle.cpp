@@ -18,7 +18,12 @@
 
 namespace {
 
-const int kMixerGDN = 0, kMixerGLA = 1;
+const int kMixerGDN = 0, kMixerGLA = 1, kMixerKDA = 3;
+
+// Per-key-channel decay (GLA, KDA) versus one decay per head (GDN, scalar).
+bool vector_decay(int mixer) { return mixer == kMixerGLA || mixer == kMixerKDA; }
+// Delta correction w = beta * (v - d.k) (GDN, KDA).
+bool delta_rule(int mixer) { return mixer == kMixerGDN || mixer == kMixerKDA; }
 const int kRoundSR = 1;
 
 int qmax(int bits) { return (1 << (bits - 1)) - 1; }  // r = 2^(b-1) - 1
@@ -225,7 +230,9 @@ static void quantize_row(const oracle_cfg* c, int bits, uint32_t key, int i,
 // precision.  Update forms: Gated DeltaNet S' = a S (I - b k k^T) + b v k^T
 // (Prop. "decaying error": unit keys, 0 < b < 2); GLA S' = S diag(alpha) +
 // v k^T; scalar decay S' = a S + dt v k^T (Prop. "repeated quantization",
-// animation details).  Readout o = S' q from the unquantized S'.
+// animation details); KDA (Table 1's "KDA": per-channel decay with delta
+// correction, the same proposition's vector gates) S' = S diag(alpha)
+// (I - b k k^T) + b v k^T.  Readout o = S' q from the unquantized S'.
 // ---------------------------------------------------------------------------
 
 void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
@@ -241,14 +248,14 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
     for (int j = 0; j < dk; ++j) {
       const float code = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j);
       const float s = scales[(size_t)i * ng + j / G];
-      if (c->mixer == kMixerGLA)
+      if (vector_decay(c->mixer))
         d[j] = (code * s) * alpha[j];
       else
         d[j] = code * (s * alpha[0]);
     }
     // write weight
     float w;
-    if (c->mixer == kMixerGDN) {
+    if (delta_rule(c->mixer)) {
       const float u = oracle_dot(d.data(), k, dk);
       w = beta * (v[i] - u);
     } else if (c->mixer == kMixerGLA) {
@@ -274,9 +281,9 @@ void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
   for (int i = 0; i < dv; ++i) {
     float* row = S + (size_t)i * dk;
     for (int j = 0; j < dk; ++j)
-      d[j] = row[j] * (c->mixer == kMixerGLA ? alpha[j] : alpha[0]);
+      d[j] = row[j] * (vector_decay(c->mixer) ? alpha[j] : alpha[0]);
     float w;
-    if (c->mixer == kMixerGDN) {
+    if (delta_rule(c->mixer)) {
       const float u = oracle_dot(d.data(), k, dk);
       w = beta * (v[i] - u);
     } else if (c->mixer == kMixerGLA) {
@@ -321,7 +328,7 @@ void oracle_step(const oracle_cfg* c, const uint8_t* head_bits, uint8_t* codes,
                  float* scales, const float* q, const float* k, const float* v,
                  const float* alpha, const float* beta, float* o, uint64_t step) {
   const int dk = c->dk, dv = c->dv, ng = dk / c->G;
-  const int na = (c->mixer == kMixerGLA) ? dk : 1;
+  const int na = vector_decay(c->mixer) ? dk : 1;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
@@ -335,7 +342,7 @@ void oracle_step(const oracle_cfg* c, const uint8_t* head_bits, uint8_t* codes,
 void oracle_step_fp32(const oracle_cfg* c, float* S, const float* q, const float* k,
                       const float* v, const float* alpha, const float* beta, float* o) {
   const int dk = c->dk, dv = c->dv;
-  const int na = (c->mixer == kMixerGLA) ? dk : 1;
+  const int na = vector_decay(c->mixer) ? dk : 1;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;

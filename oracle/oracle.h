@@ -32,7 +32,7 @@ extern "C" {
 
 typedef struct {
   int32_t B, H, dk, dv, G;
-  int32_t mixer;    /* 0 Gated DeltaNet, 1 GLA, 2 scalar decay (Mamba2) */
+  int32_t mixer;    /* 0 Gated DeltaNet, 1 GLA, 2 scalar decay (Mamba2), 3 KDA */
   int32_t rounding; /* 0 round-to-nearest-even, 1 stochastic            */
   uint64_t seed;
   uint32_t layer;
@@ -60,7 +60,8 @@ int oracle_get_code(const uint8_t* head_codes, int bits, int64_t e);
 void oracle_set_code(uint8_t* head_codes, int bits, int64_t e, int code);
 
 /* ---- one head (b, h): buffers point at that head's data ---- */
-/* alpha: 1 value (GDN, scalar) or dk values (GLA); beta: GDN beta / dt.
+/* alpha: 1 value (GDN, scalar) or dk values (GLA, KDA); beta: beta (GDN,
+ * KDA) / dt (scalar), unused for GLA.
  * o, pre, xval may be NULL.  pre receives S' [dv][dk] before requantizing;
  * xval receives the pre-rounding value per element (RTN: the exact product
  * S'*inv; SR: fma(S', inv, u)). */

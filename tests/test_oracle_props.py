@@ -13,7 +13,7 @@ on the LoReS blog ("LoReS: State Quantization"):
 import numpy as np
 import pytest
 
-GDN, GLA, SCALAR = 0, 1, 2
+GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR = 0, 1
 
 
@@ -172,7 +172,7 @@ def test_batch_wrappers_match_per_head(oracle):
                                    atol=1e-5)
 
 
-@pytest.mark.parametrize("mixer", [GDN, GLA, SCALAR])
+@pytest.mark.parametrize("mixer", [GDN, GLA, SCALAR, KDA])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quantized_step_updates_the_stored_state(oracle, mixer, bits):
     """Fig. 1 and "LoReS: State Quantization": the step reads the stored
@@ -191,6 +191,12 @@ def test_quantized_step_updates_the_stored_state(oracle, mixer, bits):
             alpha = rng.uniform(0.8, 1.0, dk).astype(np.float32)
             beta = 0.0
             want = prev @ np.diag(alpha.astype(np.float64)) + np.outer(v, k).astype(np.float64)
+        elif mixer == KDA:
+            alpha = rng.uniform(0.8, 1.0, dk).astype(np.float32)
+            beta = float(np.float32(rng.uniform(0.1, 1.5)))
+            k64 = k.astype(np.float64)
+            want = prev @ np.diag(alpha.astype(np.float64)) @ (np.eye(dk) - beta * np.outer(k64, k64)) \
+                + beta * np.outer(v.astype(np.float64), k64)
         else:
             alpha = np.float32([rng.uniform(0.8, 1.0)])
             beta = float(np.float32(rng.uniform(0.1, 1.5)))
@@ -200,3 +206,35 @@ def test_quantized_step_updates_the_stored_state(oracle, mixer, bits):
         tol = 2e-6 * max(1.0, np.abs(want).max())
         assert np.max(np.abs(pre - want)) <= tol
         assert np.max(np.abs(o - want @ q.astype(np.float64))) <= 8 * tol
+
+
+@pytest.mark.parametrize("rounding", [RTN, SR])
+def test_decaying_error_bound_vector_gates(oracle, rounding):
+    """Prop. "decaying error" with vector gates |alpha_t|_inf <= alpha < 1 and
+    delta correction (KDA): the accumulated error stays under the geometric
+    sum of fresh errors."""
+    rng = np.random.default_rng(63 + rounding)
+    dk = dv = 32
+    c = oracle.cfg(1, 1, dk, dv, 16, mixer=KDA, rounding=rounding, seed=4)
+    S0 = (rng.standard_normal((dv, dk)) * 0.5).astype(np.float32)
+    codes, scales, _ = oracle.head_quantize(c, 0, 0, 4, S0, step=0)
+    Shat = oracle.head_dequantize(c, 4, codes, scales).astype(np.float64)
+    S = S0.astype(np.float64)
+    amax = 0.95
+    terms = [np.linalg.norm(Shat - S)]
+    for t in range(1, 41):
+        k, q = _unit(rng, dk), _unit(rng, dk)
+        v = rng.standard_normal(dv).astype(np.float32)
+        al = rng.uniform(0.6, amax, dk).astype(np.float32)
+        beta = float(np.float32(rng.uniform(0.05, 1.95)))
+        k64 = k.astype(np.float64)
+        M = np.diag(al.astype(np.float64)) @ (np.eye(dk) - beta * np.outer(k64, k64))
+        prev = Shat
+        _, pre, _ = oracle.head_step(c, 0, 0, 4, codes, scales, q, k, v, al, beta, step=t,
+                                     want_pre=True)
+        Shat = oracle.head_dequantize(c, 4, codes, scales).astype(np.float64)
+        S = S @ M + beta * np.outer(v.astype(np.float64), k64)
+        eta = np.linalg.norm(pre.astype(np.float64) - (prev @ M + beta * np.outer(v, k64)))
+        assert eta <= 1e-5 * max(1.0, np.linalg.norm(prev))
+        terms = [amax * e for e in terms] + [np.linalg.norm(Shat - pre.astype(np.float64)) + eta]
+        assert np.linalg.norm(Shat - S) <= sum(terms) * (1 + 1e-9) + 1e-12

@@ -13,7 +13,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-GDN, GLA, SCALAR = 0, 1, 2
+GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "gdn_2x2_worked.txt")
 
 
@@ -58,12 +58,16 @@ def _fp64_step(mixer, S, q, k, v, alpha, beta):
         Sn = a * S @ (np.eye(len(k)) - b * np.outer(k64, k64)) + b * np.outer(v64, k64)
     elif mixer == GLA:
         Sn = S @ np.diag(alpha.astype(np.float64)) + np.outer(v64, k64)
+    elif mixer == KDA:
+        b = float(beta)
+        Sn = S @ np.diag(alpha.astype(np.float64)) @ (np.eye(len(k)) - b * np.outer(k64, k64)) \
+            + b * np.outer(v64, k64)
     else:
         Sn = float(alpha[0]) * S + float(beta) * np.outer(v64, k64)
     return Sn, Sn @ q64
 
 
-@pytest.mark.parametrize("mixer", [GDN, GLA, SCALAR])
+@pytest.mark.parametrize("mixer", [GDN, GLA, SCALAR, KDA])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (64, 48), (128, 128)])
 def test_fp32_recurrence_tracks_float64_matrix_form(oracle, mixer, dk, dv):
     rng = np.random.default_rng(10 + mixer)
@@ -73,10 +77,10 @@ def test_fp32_recurrence_tracks_float64_matrix_form(oracle, mixer, dk, dv):
     for t in range(40):
         q, k = _rand_unit(rng, dk), _rand_unit(rng, dk)
         v = rng.standard_normal(dv).astype(np.float32)
-        if mixer == GLA:
+        if mixer in (GLA, KDA):
             alpha = (1 / (1 + np.exp(-(rng.standard_normal(dk) + 3)))) ** (1 / 16)
             alpha = alpha.astype(np.float32)
-            beta = 0.0
+            beta = 0.0 if mixer == GLA else float(np.float32(1 / (1 + math.exp(-rng.standard_normal()))))
         else:
             alpha = np.float32([math.exp(-math.log1p(math.exp(rng.standard_normal() - 4)))])
             beta = float(np.float32(1 / (1 + math.exp(-rng.standard_normal()))))
@@ -230,3 +234,35 @@ def test_dot_error_bound_and_exact_cases(oracle):
         e = np.zeros(n, np.float32)
         e[j] = 1
         assert oracle.dot(x, e) == x[j]
+
+
+def test_kda_reduces_to_delta_rule_and_to_gla(oracle):
+    """KDA (per-channel decay + delta correction; LoReS Table 1 "KDA") with a
+    uniform gate is the Gated DeltaNet step, and with beta = 0 it is the GLA
+    decay alone (GLA's step with v = 0): bit-identical in FP32 and quantized."""
+    rng = np.random.default_rng(41)
+    dk, dv = 64, 32
+    S0 = rng.standard_normal((dv, dk)).astype(np.float32)
+    q, k = _rand_unit(rng, dk), _rand_unit(rng, dk)
+    v = rng.standard_normal(dv).astype(np.float32)
+    a = np.float32(0.9375)
+    b = float(np.float32(0.625))
+    ck, cg = oracle.cfg(1, 1, dk, dv, 32, mixer=KDA), oracle.cfg(1, 1, dk, dv, 32, mixer=GDN)
+    X, Y = S0.copy(), S0.copy()
+    ox = oracle.head_step_fp32(ck, X, q, k, v, np.full(dk, a, np.float32), b)
+    oy = oracle.head_step_fp32(cg, Y, q, k, v, np.float32([a]), b)
+    # c*(s*a) and (c*s)*a differ in rounding, so compare the FP32 form (S*a both ways)
+    assert np.array_equal(X, Y) and np.array_equal(ox, oy)
+    al = rng.uniform(0.8, 1.0, dk).astype(np.float32)
+    cl = oracle.cfg(1, 1, dk, dv, 32, mixer=GLA)
+    X, Y = S0.copy(), S0.copy()
+    oracle.head_step_fp32(ck, X, q, k, v, al, 0.0)
+    oracle.head_step_fp32(cl, Y, q, k, np.zeros(dv, np.float32), al, 0.0)
+    assert np.array_equal(X, Y)
+    for bits in (4, 8):
+        codes, scales, _ = oracle.head_quantize(ck, 0, 0, bits, S0, 0)
+        c1, s1, c2, s2 = codes.copy(), scales.copy(), codes.copy(), scales.copy()
+        o1, _, _ = oracle.head_step(ck, 0, 0, bits, c1, s1, q, k, v, al, 0.0, step=1)
+        o2, _, _ = oracle.head_step(cl, 0, 0, bits, c2, s2, q, k, np.zeros(dv, np.float32), al,
+                                    0.0, step=1)
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2) and np.array_equal(o1, o2)

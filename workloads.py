@@ -22,7 +22,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-GDN, GLA, SCALAR = 0, 1, 2
+GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR = 0, 1
 
 # tensor ids for the seed sequence
@@ -69,6 +69,9 @@ WORKLOADS = {
     # (slowest decay) INT8, the rest INT4; group 64; SR.
     4: Workload(4, "mamba2_24x_b512_h32_p64_n128_int8int4_g64_sr", SCALAR, 512, 32, 128, 64, 64,
                 256, 32, SR, "rank_half", layers=24),
+    # KDA (per-key-channel decay with delta correction) at the GLA shape: alpha_j as GLA's,
+    # beta as Gated DeltaNet's; INT8, group 64, SR.
+    5: Workload(5, "kda_b256_h16_d128_int8_g64_sr", KDA, 256, 16, 128, 128, 64, 512, 32, SR, "int8"),
 }
 
 
@@ -114,16 +117,19 @@ def head_a(w: Workload, seed: int = 0, layer: int = 0) -> np.ndarray:
 def step_inputs(w: Workload, t: int, seed: int = 0, layer: int = 0):
     """Inputs of input step t: (q, k, v, alpha, beta), float32, library layout.
 
-    q, k [B][H][dk]; v [B][H][dv]; alpha [B][H] or [B][H][dk] (GLA);
-    beta [B][H] (GDN beta, scalar-decay dt) or None (GLA)."""
+    q, k [B][H][dk]; v [B][H][dv]; alpha [B][H] or [B][H][dk] (GLA, KDA);
+    beta [B][H] (GDN and KDA beta, scalar-decay dt) or None (GLA)."""
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
     q = _unit(_normal(_rng(seed, w.wid, _Q, t, layer), (B, H, dk)))
     k = _unit(_normal(_rng(seed, w.wid, _K, t, layer), (B, H, dk)))
     v = _normal(_rng(seed, w.wid, _V, t, layer), (B, H, dv))
-    if w.mixer == GLA:
+    if w.mixer in (GLA, KDA):
         z = _normal(_rng(seed, w.wid, _ALPHA, t, layer), (B, H, dk)).astype(np.float64) + 3.0
         alpha = ((1.0 / (1.0 + np.exp(-z))) ** (1.0 / 16.0)).astype(np.float32)
-        return q, k, v, alpha, None
+        if w.mixer == GLA:
+            return q, k, v, alpha, None
+        zb = _normal(_rng(seed, w.wid, _BETA, t, layer), (B, H)).astype(np.float64)
+        return q, k, v, alpha, (1.0 / (1.0 + np.exp(-zb))).astype(np.float32)
     if w.mixer == SCALAR:
         dt = _rng(seed, w.wid, _DT, t, layer).uniform(0.001, 0.1, (B, H))
         a = head_a(w, seed, layer).astype(np.float64)
