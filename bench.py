@@ -56,6 +56,14 @@ def measured_traffic(workload_name: str):
     return e["hbm_bytes_per_launch"]
 
 
+def gate_bytes(w) -> int:
+    """alpha (one per head, or one per key channel for GLA and KDA) and beta
+    (absent for GLA)."""
+    import workloads as W
+    alpha = 4 * w.dk if w.mixer in (W.GLA, W.KDA) else 4
+    return alpha + (0 if w.mixer == W.GLA else 4)
+
+
 def algorithmic_bytes(w, hb) -> int:
     """Bytes one step must move: each head's codes and scales read and written
     once, q, k, v, o, and the gates (alpha per head or per key channel, beta)."""
@@ -63,13 +71,12 @@ def algorithmic_bytes(w, hb) -> int:
     for h in range(w.H):
         state = w.dv * w.dk * int(hb[h]) // 8 + w.dv * (w.dk // w.G) * 4
         io = 4 * (2 * w.dk + 2 * w.dv)
-        gates = 4 * w.dk if w.mixer == 1 else 8
-        per_b += 2 * state + io + gates
+        per_b += 2 * state + io + gate_bytes(w)
     return per_b * w.B
 
 
 def fp32_bytes(w) -> int:
-    per_head = 2 * w.dv * w.dk * 4 + 4 * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mixer == 1 else 8)
+    per_head = 2 * w.dv * w.dk * 4 + 4 * (2 * w.dk + 2 * w.dv) + gate_bytes(w)
     return per_head * w.B * w.H
 
 
@@ -91,7 +98,7 @@ def cpu_baseline(w, hb, seconds: float):
         if (b, h) not in states:
             states[(b, h)] = oracle.head_quantize(c, b, h, int(hb[h]), S0, 0)[:2]
         codes, scales = states[(b, h)]
-        a = alpha[b, h] if w.mixer == W.GLA else np.float32([alpha[b, h]])
+        a = alpha[b, h] if w.mixer in (W.GLA, W.KDA) else np.float32([alpha[b, h]])
         oracle.head_step(c, b, h, int(hb[h]), codes, scales, q[b, h], k[b, h], v[b, h], a,
                          0.0 if beta is None else float(beta[b, h]), 1 + n)
         n += 1

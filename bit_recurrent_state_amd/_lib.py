@@ -18,7 +18,7 @@ QSTATE_E_UNSUPPORTED = -2
 QSTATE_E_LAUNCH = -3
 QSTATE_E_NOMEM = -4
 
-GDN, GLA, SCALAR = 0, 1, 2
+GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR = 0, 1
 
 EXPORTS = (

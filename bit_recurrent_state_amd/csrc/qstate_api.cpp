@@ -37,7 +37,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int check_config(const qstate_config* c) {
   if (!c) return QSTATE_E_INVALID;
   if (c->batch < 1 || c->heads < 1 || c->dk < 1 || c->dv < 1) return QSTATE_E_INVALID;
-  if (c->mixer < QSTATE_GDN || c->mixer > QSTATE_SCALAR) return QSTATE_E_INVALID;
+  if (c->mixer < QSTATE_GDN || c->mixer > QSTATE_KDA) return QSTATE_E_INVALID;
   if (c->fp32_state != 0 && c->fp32_state != 1) return QSTATE_E_INVALID;
   if (!c->fp32_state) {
     if (c->rounding != QSTATE_RTN && c->rounding != QSTATE_SR) return QSTATE_E_INVALID;
@@ -168,11 +168,9 @@ int qstate_step(qstate* s, const float* q, const float* k, const float* v, const
   if (!s || !q || !k || !v || !alpha) return QSTATE_E_INVALID;
   const qstate_config& c = s->cfg;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 4)) return QSTATE_E_INVALID;
-  if (c.mixer == QSTATE_GLA) {
-    if (!aligned(alpha, 16)) return QSTATE_E_INVALID;
-  } else {
-    if (!beta || !aligned(alpha, 4) || !aligned(beta, 4)) return QSTATE_E_INVALID;
-  }
+  const bool vector_gate = c.mixer == QSTATE_GLA || c.mixer == QSTATE_KDA;
+  if (!aligned(alpha, vector_gate ? 16 : 4)) return QSTATE_E_INVALID;
+  if (c.mixer != QSTATE_GLA && (!beta || !aligned(beta, 4))) return QSTATE_E_INVALID;
   if (o && !aligned(o, 4)) return QSTATE_E_INVALID;
   qs::KParams p = base_params(s);
   p.q = q;

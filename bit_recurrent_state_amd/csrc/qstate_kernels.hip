@@ -43,7 +43,10 @@ namespace {
 
 constexpr int kThreads = 64;  // one wave per workgroup
 constexpr int kPrefetch = 4;  // row iterations whose loads are in flight ahead of compute
-constexpr int kGDN = 0, kGLA = 1, kScalar = 2;
+constexpr int kGDN = 0, kGLA = 1, kScalar = 2, kKDA = 3;
+// per-key-channel decay (GLA, KDA) and the delta-rule write weight (GDN, KDA)
+constexpr bool vector_decay(int m) { return m == kGLA || m == kKDA; }
+constexpr bool delta_rule(int m) { return m == kGDN || m == kKDA; }
 
 // ---------------------------------------------------------------------------
 // Counter-based random bits (semantics in include/qstate.h).
@@ -387,14 +390,14 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
   loadv(p.k + (size_t)sl.head * DK + col0, kk);
   loadv(p.q + (size_t)sl.head * DK + col0, qq);
   float alpha_s = 0.0f, beta = 0.0f;
-  if constexpr (MIXER == kGLA) {
+  if constexpr (vector_decay(MIXER)) {
     loadv(p.alpha + (size_t)sl.head * DK + col0, al);
   } else {
 #pragma unroll
     for (int j = 0; j < E; ++j) al[j] = 0.0f;
     alpha_s = p.alpha[sl.head];
-    beta = p.beta[sl.head];
   }
+  if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
   asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
 
   // Every lane always loads an in-range row: rows past the slice (the last
@@ -434,7 +437,7 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
       unpack16<BITS>(w, d);
       if constexpr (E == 32) unpack16<BITS>(w + 2, d + 16);
       // decayed dequantized values (exactly the rounded c*(s*alpha) / (c*s)*alpha_j)
-      if constexpr (MIXER == kGLA) {
+      if constexpr (vector_decay(MIXER)) {
         const float nb0 = -bias * s_0, nb1 = -bias * s_1;
 #pragma unroll
         for (int j = 0; j < E; ++j)
@@ -447,7 +450,7 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
       }
       // write weight
       float wt;
-      if constexpr (MIXER == kGDN) {
+      if constexpr (delta_rule(MIXER)) {
         const float u = row_sum<LPR>(lane_dot(d, kk));
         wt = beta * (vrow - u);
       } else if constexpr (MIXER == kGLA) {
@@ -498,14 +501,14 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
   loadv(p.k + (size_t)sl.head * DK + col0, kk);
   loadv(p.q + (size_t)sl.head * DK + col0, qq);
   float alpha_s = 0.0f, beta = 0.0f;
-  if constexpr (MIXER == kGLA) {
+  if constexpr (vector_decay(MIXER)) {
     loadv(p.alpha + (size_t)sl.head * DK + col0, al);
   } else {
 #pragma unroll
     for (int j = 0; j < E; ++j) al[j] = 0.0f;
     alpha_s = p.alpha[sl.head];
-    beta = p.beta[sl.head];
   }
+  if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
   asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
   // branch-free loads of in-range rows (see step_quant_head)
   auto load = [&](int it) {
@@ -531,9 +534,9 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
       const float vrow = ring[k].v;
       float d[E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) d[j] = ring[k].x[j] * (MIXER == kGLA ? al[j] : alpha_s);
+      for (int j = 0; j < E; ++j) d[j] = ring[k].x[j] * (vector_decay(MIXER) ? al[j] : alpha_s);
       float wt;
-      if constexpr (MIXER == kGDN) {
+      if constexpr (delta_rule(MIXER)) {
         const float u = row_sum<LPR>(lane_dot(d, kk));
         wt = beta * (vrow - u);
       } else if constexpr (MIXER == kGLA) {
@@ -690,6 +693,7 @@ hipError_t launch_quant(Op op, int mixer, int sr, const KParams& p, hipStream_t 
   }
     QS_STEP(kGDN, false) QS_STEP(kGDN, true) QS_STEP(kGLA, false)
     QS_STEP(kGLA, true) QS_STEP(kScalar, false) QS_STEP(kScalar, true)
+    QS_STEP(kKDA, false) QS_STEP(kKDA, true)
 #undef QS_STEP
     return hipErrorInvalidValue;
   }
@@ -720,6 +724,7 @@ hipError_t launch_dk(Op op, int mixer, int sr, int fp32, const KParams& p, hipSt
         case kGDN: step_fp32_kernel<kGDN, DK><<<grid, block, 0, s>>>(p); break;
         case kGLA: step_fp32_kernel<kGLA, DK><<<grid, block, 0, s>>>(p); break;
         case kScalar: step_fp32_kernel<kScalar, DK><<<grid, block, 0, s>>>(p); break;
+        case kKDA: step_fp32_kernel<kKDA, DK><<<grid, block, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
       }
       return hipGetLastError();

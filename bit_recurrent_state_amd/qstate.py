@@ -13,10 +13,10 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import GDN, GLA, RTN, SCALAR, SR, QStateConfig, check, lib
+from ._lib import GDN, GLA, KDA, RTN, SCALAR, SR, QStateConfig, check, lib
 
 __all__ = [
-    "GDN", "GLA", "SCALAR", "RTN", "SR", "Config", "QState",
+    "GDN", "GLA", "SCALAR", "KDA", "RTN", "SR", "Config", "QState",
     "qstate_state_bytes", "qstate_create", "qstate_load_fp32", "qstate_step",
     "qstate_readout", "qstate_store_fp32", "qstate_get_step", "qstate_set_step",
     "qstate_destroy", "qstate_bits_by_decay",
@@ -105,7 +105,7 @@ def qstate_load_fp32(h, S: torch.Tensor, cfg: Config, stream=None):
 
 def qstate_step(h, cfg: Config, q, k, v, alpha, beta=None, o=None, stream=None):
     bh = cfg.batch * cfg.heads
-    na = bh * cfg.dk if cfg.mixer == GLA else bh
+    na = bh * cfg.dk if cfg.mixer in (GLA, KDA) else bh
     args = (
         _dev(q, "q", torch.float32, bh * cfg.dk), _dev(k, "k", torch.float32, bh * cfg.dk),
         _dev(v, "v", torch.float32, bh * cfg.dv), _dev(alpha, "alpha", torch.float32, na),

@@ -30,15 +30,17 @@
  *  row i (0 <= i < dv), key column j (0 <= j < dk), group g = j / G:
  *   1. decayed dequantized row
  *        GDN, SCALAR: d_j = c_ij * (s_ig * alpha)
- *        GLA:         d_j = (c_ij * s_ig) * alpha_j
+ *        GLA, KDA:    d_j = (c_ij * s_ig) * alpha_j
  *        (FP32 state: d_j = S_ij * alpha   or   S_ij * alpha_j)
  *   2. write weight
- *        GDN:    u = dot(d, k);  w = beta * (v_i - u)
- *        GLA:    w = v_i
- *        SCALAR: w = beta * v_i          (beta carries Mamba2's dt)
+ *        GDN, KDA: u = dot(d, k);  w = beta * (v_i - u)
+ *        GLA:      w = v_i
+ *        SCALAR:   w = beta * v_i        (beta carries Mamba2's dt)
  *   3. S'_ij = fma(w, k_j, d_j)
  *      so GDN computes S' = alpha S (I - beta k k^T) + beta v k^T,
- *      GLA S' = S diag(alpha) + v k^T, SCALAR S' = alpha S + dt v k^T.
+ *      GLA S' = S diag(alpha) + v k^T, SCALAR S' = alpha S + dt v k^T,
+ *      KDA S' = S diag(alpha) (I - beta k k^T) + beta v k^T (LoReS blog,
+ *      Table 1 "KDA"; vector gates of Prop. "decaying error").
  *   4. o_i = dot(S'_i, q)       (from the full-precision S', before requant)
  *   5. m = max_{j in g} |S'_ij|;  m == 0: s' = 0, inv = 0, codes 0;
  *      else s' = m / r (correctly rounded), inv = the largest float with
@@ -67,8 +69,8 @@
  * Layout (all device buffers are caller-owned, 16-byte aligned, contiguous):
  *   q, k            float [B][H][dk]
  *   v, o            float [B][H][dv]
- *   alpha           float [B][H]      (GDN, SCALAR)  or  [B][H][dk] (GLA)
- *   beta            float [B][H]      (GDN: beta, SCALAR: dt; GLA: unused)
+ *   alpha           float [B][H]      (GDN, SCALAR)  or  [B][H][dk] (GLA, KDA)
+ *   beta            float [B][H]      (GDN, KDA: beta, SCALAR: dt; GLA: unused)
  *   codes           heads in (b, h) order; head (b,h) starts at byte
  *                   b*P + sum_{h'<h} dv*dk*n_{h'}/8, P = sum_h dv*dk*n_h/8.
  *                   Row-major [dv][dk] inside a head.  INT8: int8 two's
@@ -76,6 +78,9 @@
  *                   (i*dk + j)/2 holds even j in bits 0..3, odd j in 4..7.
  *   scales          float [B][H][dv][dk/G]
  *   FP32 state      float [B][H][dv][dk]  (fp32_state = 1)
+ *
+ * Range: state magnitudes stay below 2^120 (far beyond any FP32 recurrence
+ * that does not overflow within a few steps).
  *
  * Ownership: the library never allocates or frees device memory; a handle
  * owns only host memory.  The state is updated in place.  o must not alias
@@ -108,7 +113,8 @@ enum {
 typedef enum {
   QSTATE_GDN = 0,    /* S' = a S (I - b k k^T) + b v k^T   (Gated DeltaNet) */
   QSTATE_GLA = 1,    /* S' = S diag(alpha[dk]) + v k^T     (beta unused)    */
-  QSTATE_SCALAR = 2  /* S' = a S + b v k^T   (Mamba2 with b = dt; RetNet)   */
+  QSTATE_SCALAR = 2, /* S' = a S + b v k^T   (Mamba2 with b = dt; RetNet)   */
+  QSTATE_KDA = 3     /* S' = S diag(alpha[dk]) (I - b k k^T) + b v k^T      */
 } qstate_mixer;
 
 typedef enum { QSTATE_RTN = 0, QSTATE_SR = 1 } qstate_rounding;
@@ -148,8 +154,8 @@ int qstate_create(const qstate_config* cfg, void* codes_dev, void* scales_dev,
 int qstate_load_fp32(qstate* h, const float* S_dev, void* stream);
 
 /* The decode step (steps 1-6 above) for every head, in place; o may be NULL.
- * alpha: [B][H] (GDN, SCALAR) or [B][H][dk] (GLA); beta: [B][H] (GDN,
- * SCALAR), ignored for GLA.  Increments the step counter. */
+ * alpha: [B][H] (GDN, SCALAR) or [B][H][dk] (GLA, KDA); beta: [B][H] (GDN,
+ * SCALAR, KDA), ignored for GLA.  Increments the step counter. */
 int qstate_step(qstate* h, const float* q, const float* k, const float* v,
                 const float* alpha, const float* beta, float* o, void* stream);
 

@@ -115,7 +115,7 @@ class Run:
         return off, n
 
     def _alpha_head(self, alpha, b, h):
-        return alpha[b, h] if self.w.mixer == W.GLA else np.float32([alpha[b, h]])
+        return alpha[b, h] if self.w.mixer in (W.GLA, W.KDA) else np.float32([alpha[b, h]])
 
     def _beta_head(self, beta, b, h):
         return 0.0 if beta is None else float(beta[b, h])

@@ -59,6 +59,11 @@ def test_config3_gla_every_head(rounding):
     _run(W.WORKLOADS[3].scaled(B=3), 10, rounding=rounding)
 
 
+@pytest.mark.parametrize("rounding", [W.RTN, W.SR])
+def test_kda_every_head(rounding):
+    _run(W.WORKLOADS[5].scaled(B=3), 10, rounding=rounding)
+
+
 @pytest.mark.parametrize("layer", [0, 5])
 def test_config4_scalar_decay_layers(layer):
     _run(W.WORKLOADS[4].scaled(B=3), 8, layer=layer)
@@ -73,6 +78,8 @@ RAGGED = [
     (W.SCALAR, W.RTN, 128, 1, 64, [8, 4]),
     (W.SCALAR, W.SR, 256, 70, 16, [4, 8]),
     (W.GDN, W.SR, 128, 129, 128, [4]),
+    (W.KDA, W.SR, 64, 53, 32, [8, 4]),
+    (W.KDA, W.RTN, 256, 19, 64, [4, 8, 8]),
 ]
 
 
@@ -83,7 +90,7 @@ def test_ragged_shapes(mixer, rounding, dk, dv, G, bits):
     _run(w, 6, hb=np.array(bits, np.uint8), seed=7)
 
 
-@pytest.mark.parametrize("mixer", [W.GDN, W.GLA, W.SCALAR])
+@pytest.mark.parametrize("mixer", [W.GDN, W.GLA, W.SCALAR, W.KDA])
 def test_fp32_state_is_the_fp32_recurrence(mixer):
     """The unquantized run equals the reference FP32 recurrence bit for bit."""
     w = W.Workload(95, f"fp32_m{mixer}", mixer, 4, 8, 128, 128, 32, 0, 48, W.RTN, "int8")
@@ -92,7 +99,7 @@ def test_fp32_state_is_the_fp32_recurrence(mixer):
     r.warmup_and_import()
 
 
-FULL = {1: 3, 2: 2, 3: 2, 4: 2}
+FULL = {1: 3, 2: 2, 3: 2, 4: 2, 5: 2}
 
 
 @pytest.mark.parametrize("wid", sorted(FULL))
