@@ -20,7 +20,7 @@ SRC = os.path.join(HERE, "oracle.cpp")
 LIB = os.path.join(HERE, "liboracle.so")
 
 GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
-RTN, SR = 0, 1
+RTN, SR, BDR = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -63,6 +63,7 @@ def lib():
             "oracle_group_scale": (None, [f32, i32, _P, _P]),
             "oracle_round_rtn": (i32, [f32, f32]),
             "oracle_round_sr": (i32, [f32, f32, u32]),
+            "oracle_round_bdr": (i32, [f32, f32, f32, f32, i32]),
             "oracle_codes_bytes": (ctypes.c_size_t, [cp, _P]),
             "oracle_head_offset": (ctypes.c_size_t, [cp, _P, i32, i32]),
             "oracle_get_code": (i32, [_P, i32, ctypes.c_int64]),
@@ -151,6 +152,10 @@ def round_rtn(x: float, inv: float) -> int:
 
 def round_sr(x: float, inv: float, r16: int) -> int:
     return lib().oracle_round_sr(x, inv, r16)
+
+
+def round_bdr(x: float, inv: float, s_new: float, prev: float, r: int) -> int:
+    return lib().oracle_round_bdr(x, inv, s_new, prev, r)
 
 
 def codes_bytes(c: Cfg, head_bits=None) -> int:

@@ -24,7 +24,7 @@ const int kMixerGDN = 0, kMixerGLA = 1, kMixerKDA = 3;
 bool vector_decay(int mixer) { return mixer == kMixerGLA || mixer == kMixerKDA; }
 // Delta correction w = beta * (v - d.k) (GDN, KDA).
 bool delta_rule(int mixer) { return mixer == kMixerGDN || mixer == kMixerKDA; }
-const int kRoundSR = 1;
+const int kRoundSR = 1, kRoundBDR = 2;
 
 int qmax(int bits) { return (1 << (bits - 1)) - 1; }  // r = 2^(b-1) - 1
 
@@ -142,6 +142,24 @@ int oracle_round_sr(float x, float inv, uint32_t r16) {
   return (int)std::floor(std::fma(x, inv, u));
 }
 
+// Bounded directional rounding ("Preserving Updates", abstract: reversed
+// elements are rounded toward their update, with no extra storage).  The
+// element's stored value was prev = c*s before the step and its full-precision
+// update takes it to x; round-to-nearest gives the code n whose stored value is
+// n*s_new.  When prev lies strictly between n*s_new and x, the stored value
+// moved against the update: take one grid step toward the update (the other
+// neighbour of x*inv, so the rounding error stays below one step), then clamp
+// to [-r, r].  A lost update (n*s_new == prev) or no update (x == prev) is
+// left as rounded.
+int oracle_round_bdr(float x, float inv, float s_new, float prev, int r) {
+  int n = oracle_round_rtn(x, inv);
+  const float stored = (float)n * s_new;
+  const bool up = x > prev, down = x < prev;
+  if (up && stored < prev) n += 1;
+  if (down && stored > prev) n -= 1;
+  return std::max(-r, std::min(r, n));
+}
+
 // ---------------------------------------------------------------------------
 // Layout: codes of head (b, h) start at b*P + sum_{h'<h} dv*dk*bits_h'/8.
 // INT8 codes are int8; INT4 codes are two's-complement nibbles, even element
@@ -193,9 +211,11 @@ void oracle_set_code(uint8_t* codes, int bits, int64_t e, int code) {
 // is taken from the state being stored, 4/4 "noisy" scale).
 // ---------------------------------------------------------------------------
 
+// prev: the row's stored values before the step (BDR); NULL for an import,
+// where BDR has nothing to compare with and rounds to nearest.
 static void quantize_row(const oracle_cfg* c, int bits, uint32_t key, int i,
-                         const float* row, uint8_t* codes, float* scales,
-                         double* xval) {
+                         const float* row, const float* prev, uint8_t* codes,
+                         float* scales, double* xval) {
   const int dk = c->dk, G = c->G, ng = dk / G, r = qmax(bits);
   for (int g = 0; g < ng; ++g) {
     float m = 0.0f;
@@ -213,6 +233,9 @@ static void quantize_row(const oracle_cfg* c, int bits, uint32_t key, int i,
           const float u = (float)r16 * (1.0f / 65536.0f);
           xval[e] = (double)std::fma(row[j], inv, u);
         }
+      } else if (c->rounding == kRoundBDR && prev) {
+        n = oracle_round_bdr(row[j], inv, s, prev[j], r);
+        if (xval) xval[e] = (double)row[j] * (double)inv;
       } else {
         n = oracle_round_rtn(row[j], inv);
         if (xval) xval[e] = (double)row[j] * (double)inv;
@@ -242,12 +265,13 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
                       double* xval) {
   const int dk = c->dk, dv = c->dv, G = c->G, ng = dk / G;
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
-  std::vector<float> d(dk), sp(dk);
+  std::vector<float> d(dk), sp(dk), stored(dk);
   for (int i = 0; i < dv; ++i) {
     // dequantize and decay
     for (int j = 0; j < dk; ++j) {
       const float code = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j);
       const float s = scales[(size_t)i * ng + j / G];
+      stored[j] = code * s;
       if (vector_decay(c->mixer))
         d[j] = (code * s) * alpha[j];
       else
@@ -267,7 +291,7 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
     for (int j = 0; j < dk; ++j) sp[j] = std::fma(w, k[j], d[j]);
     if (o) o[i] = oracle_dot(sp.data(), q, dk);
     if (pre) std::memcpy(pre + (size_t)i * dk, sp.data(), sizeof(float) * dk);
-    quantize_row(c, bits, key, i, sp.data(), codes, scales, xval);
+    quantize_row(c, bits, key, i, sp.data(), stored.data(), codes, scales, xval);
   }
 }
 
@@ -301,7 +325,7 @@ void oracle_head_quantize(const oracle_cfg* c, int b, int h, int bits,
                           uint64_t step, double* xval) {
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
   for (int i = 0; i < c->dv; ++i)
-    quantize_row(c, bits, key, i, S + (size_t)i * c->dk, codes, scales, xval);
+    quantize_row(c, bits, key, i, S + (size_t)i * c->dk, nullptr, codes, scales, xval);
 }
 
 void oracle_head_dequantize(const oracle_cfg* c, int bits, const uint8_t* codes,

@@ -33,7 +33,8 @@ extern "C" {
 typedef struct {
   int32_t B, H, dk, dv, G;
   int32_t mixer;    /* 0 Gated DeltaNet, 1 GLA, 2 scalar decay (Mamba2), 3 KDA */
-  int32_t rounding; /* 0 round-to-nearest-even, 1 stochastic            */
+  int32_t rounding; /* 0 round-to-nearest-even, 1 stochastic,
+                       2 bounded directional (nearest for an import)     */
   uint64_t seed;
   uint32_t layer;
 } oracle_cfg;
@@ -51,6 +52,7 @@ float oracle_dot(const float* x, const float* y, int n);
 void oracle_group_scale(float m, int r, float* s, float* inv);
 int oracle_round_rtn(float x, float inv);
 int oracle_round_sr(float x, float inv, uint32_t r16);
+int oracle_round_bdr(float x, float inv, float s_new, float prev, int r);
 
 /* ---- layout ---- */
 size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* head_bits);

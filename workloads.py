@@ -23,7 +23,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
-RTN, SR = 0, 1
+RTN, SR, BDR = 0, 1, 2
 
 # tensor ids for the seed sequence
 _Q, _K, _V, _BETA, _ALPHA, _HEAD_ALPHA, _HEAD_A, _DT = range(8)
