@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized-state decode steps/s and HBM GB/s (% of peak) at B=256, INT8/INT4"
 HBM_PEAK_GBPS = 8000.0
+ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", "qstate_kernels.hip")
 
@@ -110,7 +111,7 @@ def cpu_baseline(w, hb, seconds: float):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{n} head-steps of the same workload ({w.dv}x{w.dk} heads, mixed bits, "
-                  f"{'SR' if w.rounding else 'RTN'}) in {dt:.1f} s on one host thread, "
+                  f"{ROUNDING_NAMES[w.rounding]}) in {dt:.1f} s on one host thread, "
                   f"scaled by the {w.B * w.H} heads of one step",
     }
 
@@ -121,7 +122,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--rounding", type=int, default=None, help="override: 0 RTN, 1 SR")
+    ap.add_argument("--rounding", type=int, default=None, help="override: 0 RTN, 1 SR, 2 BDR")
     ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
     ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -211,7 +212,7 @@ def main():
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "group": w.G,
             "state_bits": {str(b): int((hb == b).sum()) for b in sorted(set(hb.tolist()))},
-            "rounding": "SR" if w.rounding else "RTN", "state_instances": n_states,
+            "rounding": ROUNDING_NAMES[w.rounding], "state_instances": n_states,
             "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,
         },
         "hbm_gbps": gbps,

@@ -19,7 +19,7 @@ QSTATE_E_LAUNCH = -3
 QSTATE_E_NOMEM = -4
 
 GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
-RTN, SR = 0, 1
+RTN, SR, BDR = 0, 1, 2
 
 EXPORTS = (
     "qstate_state_bytes", "qstate_create", "qstate_load_fp32", "qstate_step",

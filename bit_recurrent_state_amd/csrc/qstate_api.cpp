@@ -40,7 +40,7 @@ int check_config(const qstate_config* c) {
   if (c->mixer < QSTATE_GDN || c->mixer > QSTATE_KDA) return QSTATE_E_INVALID;
   if (c->fp32_state != 0 && c->fp32_state != 1) return QSTATE_E_INVALID;
   if (!c->fp32_state) {
-    if (c->rounding != QSTATE_RTN && c->rounding != QSTATE_SR) return QSTATE_E_INVALID;
+    if (c->rounding < QSTATE_RTN || c->rounding > QSTATE_BDR) return QSTATE_E_INVALID;
     if (c->group < 1 || c->dk % c->group != 0) return QSTATE_E_INVALID;
     if (c->head_bits)
       for (int h = 0; h < c->heads && h < kMaxHeads; ++h)

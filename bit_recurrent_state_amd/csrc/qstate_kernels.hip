@@ -44,6 +44,7 @@ namespace {
 constexpr int kThreads = 64;  // one wave per workgroup
 constexpr int kPrefetch = 4;  // row iterations whose loads are in flight ahead of compute
 constexpr int kGDN = 0, kGLA = 1, kScalar = 2, kKDA = 3;
+constexpr int kRTN = 0, kSR = 1, kBDR = 2;  // rounding of the step
 // per-key-channel decay (GLA, KDA) and the delta-rule write weight (GDN, KDA)
 constexpr bool vector_decay(int m) { return m == kGLA || m == kKDA; }
 constexpr bool delta_rule(int m) { return m == kGDN || m == kKDA; }
@@ -251,12 +252,15 @@ __device__ __forceinline__ int32_t floor_i32(float x) {
 
 // Requantize one 16-element chunk with inverse scale inv into 16 packed codes
 // (four words for INT8, two for INT4).  block: the chunk's 16-element block
-// index in the head (stochastic rounding).
-template <int BITS, bool SR>
+// index in the head (stochastic rounding).  wprev / s_old: the chunk's codes
+// and scale before the step, s_new its new scale (bounded directional
+// rounding).
+template <int BITS, int RND>
 __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t key, uint32_t block,
+                                           const uint32_t* wprev, float s_old, float s_new,
                                            uint32_t* out) {
   uint32_t src[16];
-  if constexpr (SR) {
+  if constexpr (RND == kSR) {
     float R[16];
     block_r16(key, block, R);
     if (__builtin_expect(inv <= 0x1p100f, 1)) {
@@ -270,8 +274,32 @@ __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t 
     }
     pack16<BITS, 2>(src, out);
   } else {
+    // y = 1.5*2^23 + rint(S'*inv): the code sits in the low mantissa bits.
+    constexpr float kMagic = 12582912.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv, 12582912.0f));
+    for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv, kMagic));
+    if constexpr (RND == kBDR) {
+      // prev = c*s_old exactly as stored; the nearest code's stored value
+      // (y - magic)*s_new; where prev lies strictly between that value and
+      // S', step one code toward S' (y stays in the magic's binade, so +-1
+      // is exact), then clamp to [-r, r].
+      constexpr int R = (1 << (BITS - 1)) - 1;
+      constexpr float bias = (float)(1 << (BITS - 1));
+      float prev[16];
+      unpack16<BITS>(wprev, prev);
+      const float nb = -bias * s_old;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = __builtin_fmaf(prev[j], s_old, nb);
+        float y = __uint_as_float(src[j]);
+        const float st = (y - kMagic) * s_new;
+        const float x = sp[j];
+        if (x > pv && st < pv) y += 1.0f;
+        if (x < pv && st > pv) y -= 1.0f;
+        y = fminf(fmaxf(y, kMagic - (float)R), kMagic + (float)R);
+        src[j] = __float_as_uint(y);
+      }
+    }
     pack16<BITS, 0>(src, out);
   }
 }
@@ -279,11 +307,13 @@ __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t 
 // Requantize the lane's E elements of the updated row S' into 16 bytes of
 // codes.  LPG = 0: two groups per lane (INT4 with G = 16, one per chunk);
 // otherwise one group spanning LPG lanes.  s0/s1: the scales of the lane's
-// groups.
-template <int BITS, bool SR, int E, int LPG>
+// groups (in: before the step, used by bounded directional rounding; out:
+// the new ones).  wprev: the lane's four code words before the step.
+template <int BITS, int RND, int E, int LPG>
 __device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t key, uint32_t block0,
-                                               float& s0, float& s1) {
+                                               const uint32_t* wprev, float& s0, float& s1) {
   constexpr int R = (1 << (BITS - 1)) - 1;
+  const float so0 = s0, so1 = s1;
   float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) m0 = fmaxf(m0, fabsf(sp[j]));
@@ -301,8 +331,9 @@ __device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t ke
     s1 = s0, inv1 = inv0;
   }
   uint32_t o[4];
-  quantize16<BITS, SR>(sp, inv0, key, block0, o);
-  if constexpr (E == 32) quantize16<BITS, SR>(sp + 16, inv1, key, block0 + 1, o + 2);
+  quantize16<BITS, RND>(sp, inv0, key, block0, wprev, so0, s0, o);
+  if constexpr (E == 32)
+    quantize16<BITS, RND>(sp + 16, inv1, key, block0 + 1, wprev + 2, so1, s1, o + 2);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -364,8 +395,9 @@ struct RowIn {
   float s0, s1, v;
 };
 
-template <int MIXER, bool SR, int DK, int BITS, int G>
+template <int MIXER, int RND, int DK, int BITS, int G>
 __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl) {
+  constexpr bool SR = RND == kSR;
   using Gm = Geo<DK, BITS>;
   constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
   constexpr float bias = (float)(1 << (BITS - 1));
@@ -464,9 +496,9 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
       ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
       const float o = row_sum<LPR>(lane_dot(d, qq));
       // requantize
-      float s0, s1;
+      float s0 = s_0, s1 = s_1;
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
-      const uint4 packed = quantize_lane<BITS, SR, E, LPG>(d, key, block0, s0, s1);
+      const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
       if (store_ok) {
         *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
         if constexpr (two_groups) {
@@ -587,9 +619,11 @@ __device__ __forceinline__ void aux_quant_head(const KParams& p, const Slice sl)
       else
 #pragma unroll
         for (int j = 0; j < E; ++j) x[j] = 0.0f;
-      float s0, s1;
+      float s0 = 0.0f, s1 = 0.0f;
+      const uint32_t no_prev[4] = {0u, 0u, 0u, 0u};  // read only by BDR, never on import
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
-      const uint4 packed = quantize_lane<BITS, SR, E, LPG>(x, key, block0, s0, s1);
+      const uint4 packed =
+          quantize_lane<BITS, SR ? kSR : kRTN, E, LPG>(x, key, block0, no_prev, s0, s1);
       if (ok) {
         *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
         if constexpr (two_groups) {
@@ -628,13 +662,13 @@ __device__ __forceinline__ void aux_quant_head(const KParams& p, const Slice sl)
 // Kernels.
 // ---------------------------------------------------------------------------
 
-template <int MIXER, bool SR, int DK, int G>
+template <int MIXER, int RND, int DK, int G>
 __global__ __launch_bounds__(kThreads) void step_kernel(const KParams p) {
   const Slice sl = wave_slice(p);
   if (head_is_int8(p, sl.h))
-    step_quant_head<MIXER, SR, DK, 8, G>(p, sl);
+    step_quant_head<MIXER, RND, DK, 8, G>(p, sl);
   else
-    step_quant_head<MIXER, SR, DK, 4, G>(p, sl);
+    step_quant_head<MIXER, RND, DK, 4, G>(p, sl);
 }
 
 template <int MIXER, int DK>
@@ -683,23 +717,26 @@ __global__ __launch_bounds__(kThreads) void readout_fp32_kernel(const KParams p)
 inline dim3 grid_of(const KParams& p) { return dim3((unsigned)(p.B * p.H * p.slices)); }
 
 template <int DK, int G>
-hipError_t launch_quant(Op op, int mixer, int sr, const KParams& p, hipStream_t s) {
+hipError_t launch_quant(Op op, int mixer, int rnd, const KParams& p, hipStream_t s) {
   const dim3 grid = grid_of(p), block(kThreads);
   if (op == kStep) {
-#define QS_STEP(M, S)                                           \
-  if (mixer == M && sr == S) {                                  \
-    step_kernel<M, S, DK, G><<<grid, block, 0, s>>>(p);         \
-    return hipGetLastError();                                   \
+#define QS_STEP(M)                                                    \
+  if (mixer == M) {                                                   \
+    switch (rnd) {                                                    \
+      case kRTN: step_kernel<M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
+      case kSR: step_kernel<M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
+      case kBDR: step_kernel<M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
+      default: return hipErrorInvalidValue;                           \
+    }                                                                 \
+    return hipGetLastError();                                         \
   }
-    QS_STEP(kGDN, false) QS_STEP(kGDN, true) QS_STEP(kGLA, false)
-    QS_STEP(kGLA, true) QS_STEP(kScalar, false) QS_STEP(kScalar, true)
-    QS_STEP(kKDA, false) QS_STEP(kKDA, true)
+    QS_STEP(kGDN) QS_STEP(kGLA) QS_STEP(kScalar) QS_STEP(kKDA)
 #undef QS_STEP
     return hipErrorInvalidValue;
   }
   switch (op) {
-    case kImport:
-      if (sr)
+    case kImport:  // nothing stored before an import: BDR rounds to nearest
+      if (rnd == kSR)
         aux_kernel<kImport, true, DK, G><<<grid, block, 0, s>>>(p);
       else
         aux_kernel<kImport, false, DK, G><<<grid, block, 0, s>>>(p);
@@ -716,7 +753,7 @@ hipError_t launch_quant(Op op, int mixer, int sr, const KParams& p, hipStream_t 
 }
 
 template <int DK>
-hipError_t launch_dk(Op op, int mixer, int sr, int fp32, const KParams& p, hipStream_t s) {
+hipError_t launch_dk(Op op, int mixer, int rnd, int fp32, const KParams& p, hipStream_t s) {
   const dim3 grid = grid_of(p), block(kThreads);
   if (fp32) {
     if (op == kStep) {
@@ -736,10 +773,10 @@ hipError_t launch_dk(Op op, int mixer, int sr, int fp32, const KParams& p, hipSt
     return hipErrorInvalidValue;  // import/export of an FP32 state are plain copies
   }
   switch (p.G) {
-    case 16: return launch_quant<DK, 16>(op, mixer, sr, p, s);
-    case 32: return launch_quant<DK, 32>(op, mixer, sr, p, s);
-    case 64: return launch_quant<DK, 64>(op, mixer, sr, p, s);
-    case 128: return launch_quant<DK, 128>(op, mixer, sr, p, s);
+    case 16: return launch_quant<DK, 16>(op, mixer, rnd, p, s);
+    case 32: return launch_quant<DK, 32>(op, mixer, rnd, p, s);
+    case 64: return launch_quant<DK, 64>(op, mixer, rnd, p, s);
+    case 128: return launch_quant<DK, 128>(op, mixer, rnd, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -751,12 +788,12 @@ hipError_t launch(Op op, int mixer, int rounding, int fp32, int dk, const KParam
   if (p.slices < 1 || p.slice_rows < 1 || p.slice_rows % 32 != 0 ||
       (int64_t)p.slices * p.slice_rows < p.dv)
     return hipErrorInvalidValue;
-  const int sr = (rounding == 1 && !fp32) ? 1 : 0;
+  const int rnd = fp32 ? kRTN : rounding;
   const int f = fp32 ? 1 : 0;
   switch (dk) {
-    case 64: return launch_dk<64>(op, mixer, sr, f, p, stream);
-    case 128: return launch_dk<128>(op, mixer, sr, f, p, stream);
-    case 256: return launch_dk<256>(op, mixer, sr, f, p, stream);
+    case 64: return launch_dk<64>(op, mixer, rnd, f, p, stream);
+    case 128: return launch_dk<128>(op, mixer, rnd, f, p, stream);
+    case 256: return launch_dk<256>(op, mixer, rnd, f, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

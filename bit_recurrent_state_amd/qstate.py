@@ -13,10 +13,10 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import GDN, GLA, KDA, RTN, SCALAR, SR, QStateConfig, check, lib
+from ._lib import BDR, GDN, GLA, KDA, RTN, SCALAR, SR, QStateConfig, check, lib
 
 __all__ = [
-    "GDN", "GLA", "SCALAR", "KDA", "RTN", "SR", "Config", "QState",
+    "GDN", "GLA", "SCALAR", "KDA", "RTN", "SR", "BDR", "Config", "QState",
     "qstate_state_bytes", "qstate_create", "qstate_load_fp32", "qstate_step",
     "qstate_readout", "qstate_store_fp32", "qstate_get_step", "qstate_set_step",
     "qstate_destroy", "qstate_bits_by_decay",

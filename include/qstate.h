@@ -48,6 +48,12 @@
  *   6. RTN: code = round-half-even(S'_ij * inv)   (exact product)
  *      SR:  code = floor(fma(S'_ij, inv, u_ij)), u_ij = R16_ij * 2^-16
  *      No clamp is ever active: both stay within [-r, r].
+ *      BDR ("Preserving Updates" abstract: reversed elements are rounded
+ *      toward their update, with no extra storage): n = the RTN code,
+ *      p = c_ij * s_ig (the element's stored value before the step, one
+ *      FP32 product), t = n * s'_ig (FP32).  If S'_ij > p and t < p, n += 1;
+ *      if S'_ij < p and t > p, n -= 1; then clamp n to [-r, r].  An import
+ *      (no stored value before it) rounds to nearest.
  *   dot(x, y): 16-element chunks, each accumulated p = fma(x_j, y_j, p) from
  *   p = 0 in ascending j, then a pairwise tree over the chunk partials
  *   (((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) for dk = 128).
@@ -117,7 +123,11 @@ typedef enum {
   QSTATE_KDA = 3     /* S' = S diag(alpha[dk]) (I - b k k^T) + b v k^T      */
 } qstate_mixer;
 
-typedef enum { QSTATE_RTN = 0, QSTATE_SR = 1 } qstate_rounding;
+typedef enum {
+  QSTATE_RTN = 0, /* round to nearest, ties to even                        */
+  QSTATE_SR = 1,  /* stochastic rounding (counter-based bits)              */
+  QSTATE_BDR = 2  /* bounded directional rounding (nearest for an import)  */
+} qstate_rounding;
 
 typedef struct {
   int32_t batch;            /* B >= 1                                         */

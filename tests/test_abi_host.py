@@ -63,7 +63,7 @@ def test_state_bytes(L):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), -1), (dict(heads=0), -1), (dict(dv=0), -1), (dict(mixer=4), -1),
-    (dict(rounding=2), -1), (dict(group=48), -1), (dict(fp32_state=2), -1),
+    (dict(rounding=3), -1), (dict(group=48), -1), (dict(fp32_state=2), -1),
     (dict(dk=96, group=32), -2), (dict(dk=512, group=64), -2), (dict(heads=300), -2),
     (dict(dv=5000), -2), (dict(group=8), -2),
 ])

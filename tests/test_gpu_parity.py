@@ -64,6 +64,19 @@ def test_kda_every_head(rounding):
     _run(W.WORKLOADS[5].scaled(B=3), 10, rounding=rounding)
 
 
+@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+def test_bdr_every_head(wid):
+    """Bounded directional rounding on every recurrence, mixed bits included."""
+    _run(W.WORKLOADS[wid].scaled(B=2), 10, rounding=W.BDR)
+
+
+def test_bdr_full_size_sampled_heads():
+    w = W.WORKLOADS[2]
+    rng = np.random.default_rng(12)
+    idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
+    _run(w, 2, rounding=W.BDR, heads=sorted((i // w.H, i % w.H) for i in idx))
+
+
 @pytest.mark.parametrize("layer", [0, 5])
 def test_config4_scalar_decay_layers(layer):
     _run(W.WORKLOADS[4].scaled(B=3), 8, layer=layer)
@@ -80,6 +93,8 @@ RAGGED = [
     (W.GDN, W.SR, 128, 129, 128, [4]),
     (W.KDA, W.SR, 64, 53, 32, [8, 4]),
     (W.KDA, W.RTN, 256, 19, 64, [4, 8, 8]),
+    (W.GDN, W.BDR, 64, 37, 16, [4, 8, 4]),
+    (W.GLA, W.BDR, 256, 23, 128, [8, 4]),
 ]
 
 
