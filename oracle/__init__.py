@@ -21,6 +21,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR, BDR = 0, 1, 2
+VALUE_AXIS, KEY_AXIS = 0, 1
 
 
 def build(force: bool = False) -> str:
@@ -40,7 +41,7 @@ class Cfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("G", ctypes.c_int32), ("mixer", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("layer", ctypes.c_uint32)]
+                ("layer", ctypes.c_uint32), ("axis", ctypes.c_int32)]
 
 
 _lib = None
@@ -99,8 +100,13 @@ def _f32(a):
     return a
 
 
-def cfg(B, H, dk, dv, G, mixer=GDN, rounding=RTN, seed=0, layer=0) -> Cfg:
-    return Cfg(B, H, dk, dv, G, mixer, rounding, seed, layer)
+def cfg(B, H, dk, dv, G, mixer=GDN, rounding=RTN, seed=0, layer=0, axis=VALUE_AXIS) -> Cfg:
+    return Cfg(B, H, dk, dv, G, mixer, rounding, seed, layer, axis)
+
+
+def scales_shape(c: Cfg):
+    """Per-head scale array: [dv][dk/G] (value-axis groups) or [dv/G][dk] (key-axis)."""
+    return (c.dv // c.G, c.dk) if c.axis == KEY_AXIS else (c.dv, c.dk // c.G)
 
 
 def head_bits_array(c: Cfg, head_bits=None) -> np.ndarray:
@@ -193,7 +199,7 @@ def head_step(c: Cfg, b, h, bits, codes, scales, q, k, v, alpha, beta, step,
     assert codes.dtype == np.uint8 and codes.flags.c_contiguous
     assert scales.dtype == np.float32 and scales.flags.c_contiguous
     assert codes.size == c.dv * c.dk * bits // 8
-    assert scales.size == c.dv * (c.dk // c.G)
+    assert scales.size == int(np.prod(scales_shape(c)))
     q, k, v, alpha = _f32(q), _f32(k), _f32(v), _f32(alpha)
     assert q.size == c.dk and k.size == c.dk and v.size == c.dv
     assert alpha.size == (c.dk if c.mixer in (GLA, KDA) else 1)
@@ -219,7 +225,7 @@ def head_quantize(c: Cfg, b, h, bits, S, step, want_xval=False):
     S = _f32(S)
     assert S.size == c.dv * c.dk
     codes = np.zeros(c.dv * c.dk * bits // 8, np.uint8)
-    scales = np.zeros(c.dv * (c.dk // c.G), np.float32)
+    scales = np.zeros(int(np.prod(scales_shape(c))), np.float32)
     xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
     lib().oracle_head_quantize(ctypes.byref(c), b, h, bits, _ptr(S), _ptr(codes),
                                _ptr(scales), step, _ptr(xval))
@@ -269,7 +275,7 @@ def quantize(c: Cfg, head_bits, S, t):
     hb = head_bits_array(c, head_bits)
     S = _f32(S)
     codes = np.zeros(codes_bytes(c, hb), np.uint8)
-    scales = np.zeros((c.B, c.H, c.dv, c.dk // c.G), np.float32)
+    scales = np.zeros((c.B, c.H) + scales_shape(c), np.float32)
     lib().oracle_quantize(ctypes.byref(c), _ptr(hb), _ptr(S), _ptr(codes), _ptr(scales), t)
     return codes, scales
 

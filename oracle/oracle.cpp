@@ -25,6 +25,7 @@ bool vector_decay(int mixer) { return mixer == kMixerGLA || mixer == kMixerKDA; 
 // Delta correction w = beta * (v - d.k) (GDN, KDA).
 bool delta_rule(int mixer) { return mixer == kMixerGDN || mixer == kMixerKDA; }
 const int kRoundSR = 1, kRoundBDR = 2;
+const int kAxisKey = 1;  // scale groups along the value axis of one key column
 
 int qmax(int bits) { return (1 << (bits - 1)) - 1; }  // r = 2^(b-1) - 1
 
@@ -207,42 +208,78 @@ void oracle_set_code(uint8_t* codes, int bits, int64_t e, int code) {
 }
 
 // ---------------------------------------------------------------------------
-// Requantization of one value row (LoReS: value-axis grouping, 1/4; the scale
-// is taken from the state being stored, 4/4 "noisy" scale).
+// Requantization of a head (LoReS "Scale grouping" (1/4): a group of G state
+// elements shares one absmax scale, taken from the state being stored (4/4,
+// "noisy" scale)).  Value-axis groups, the LoReS default, are G consecutive
+// key columns of one value row: scales [dv][dk/G].  Key-axis groups, the
+// comparison in the same section (C_j of Prop. "per-channel readout error"
+// when G = dv), are G consecutive value rows of one key column: scales
+// [dv/G][dk].
 // ---------------------------------------------------------------------------
 
-// prev: the row's stored values before the step (BDR); NULL for an import,
-// where BDR has nothing to compare with and rounds to nearest.
-static void quantize_row(const oracle_cfg* c, int bits, uint32_t key, int i,
-                         const float* row, const float* prev, uint8_t* codes,
-                         float* scales, double* xval) {
-  const int dk = c->dk, G = c->G, ng = dk / G, r = qmax(bits);
-  for (int g = 0; g < ng; ++g) {
-    float m = 0.0f;
-    for (int j = g * G; j < (g + 1) * G; ++j) m = std::max(m, std::fabs(row[j]));
-    float s, inv;
-    oracle_group_scale(m, r, &s, &inv);
-    scales[(size_t)i * ng + g] = s;
-    for (int j = g * G; j < (g + 1) * G; ++j) {
-      const int64_t e = (int64_t)i * dk + j;
-      int n;
-      if (c->rounding == kRoundSR) {
-        const uint32_t r16 = oracle_sr_bits(key, (uint64_t)e);
-        n = oracle_round_sr(row[j], inv, r16);
-        if (xval) {
-          const float u = (float)r16 * (1.0f / 65536.0f);
-          xval[e] = (double)std::fma(row[j], inv, u);
-        }
-      } else if (c->rounding == kRoundBDR && prev) {
-        n = oracle_round_bdr(row[j], inv, s, prev[j], r);
-        if (xval) xval[e] = (double)row[j] * (double)inv;
-      } else {
-        n = oracle_round_rtn(row[j], inv);
-        if (xval) xval[e] = (double)row[j] * (double)inv;
+// Scales per head: dv * dk / G for either axis (G divides the grouped axis).
+static size_t head_scales(const oracle_cfg* c) {
+  if (c->axis == kAxisKey) return (size_t)(c->dv / c->G) * c->dk;
+  return (size_t)c->dv * (c->dk / c->G);
+}
+
+static size_t scale_index(const oracle_cfg* c, int i, int j) {
+  if (c->axis == kAxisKey) return (size_t)(i / c->G) * c->dk + j;
+  return (size_t)i * (c->dk / c->G) + j / c->G;
+}
+
+// Quantize one group: elements e[0..n) (indices i*dk + j into the head) of
+// S, with scale slot si.  prev: the head's stored values before the step
+// (BDR); NULL for an import, where BDR has nothing to compare with and
+// rounds to nearest.
+static void quantize_group(const oracle_cfg* c, int bits, uint32_t key,
+                           const std::vector<int64_t>& e, size_t si,
+                           const float* S, const float* prev, uint8_t* codes,
+                           float* scales, double* xval) {
+  const int r = qmax(bits);
+  float m = 0.0f;
+  for (int64_t x : e) m = std::max(m, std::fabs(S[x]));
+  float s, inv;
+  oracle_group_scale(m, r, &s, &inv);
+  scales[si] = s;
+  for (int64_t x : e) {
+    int n;
+    if (c->rounding == kRoundSR) {
+      const uint32_t r16 = oracle_sr_bits(key, (uint64_t)x);
+      n = oracle_round_sr(S[x], inv, r16);
+      if (xval) {
+        const float u = (float)r16 * (1.0f / 65536.0f);
+        xval[x] = (double)std::fma(S[x], inv, u);
       }
-      n = std::max(-r, std::min(r, n));
-      oracle_set_code(codes, bits, e, n);
+    } else if (c->rounding == kRoundBDR && prev) {
+      n = oracle_round_bdr(S[x], inv, s, prev[x], r);
+      if (xval) xval[x] = (double)S[x] * (double)inv;
+    } else {
+      n = oracle_round_rtn(S[x], inv);
+      if (xval) xval[x] = (double)S[x] * (double)inv;
     }
+    n = std::max(-r, std::min(r, n));
+    oracle_set_code(codes, bits, x, n);
+  }
+}
+
+static void quantize_head(const oracle_cfg* c, int bits, uint32_t key,
+                          const float* S, const float* prev, uint8_t* codes,
+                          float* scales, double* xval) {
+  const int dk = c->dk, dv = c->dv, G = c->G;
+  std::vector<int64_t> e(G);
+  if (c->axis == kAxisKey) {
+    for (int g = 0; g < dv / G; ++g)
+      for (int j = 0; j < dk; ++j) {
+        for (int t = 0; t < G; ++t) e[t] = (int64_t)(g * G + t) * dk + j;
+        quantize_group(c, bits, key, e, scale_index(c, g * G, j), S, prev, codes, scales, xval);
+      }
+  } else {
+    for (int i = 0; i < dv; ++i)
+      for (int g = 0; g < dk / G; ++g) {
+        for (int t = 0; t < G; ++t) e[t] = (int64_t)i * dk + g * G + t;
+        quantize_group(c, bits, key, e, scale_index(c, i, g * G), S, prev, codes, scales, xval);
+      }
   }
 }
 
@@ -263,15 +300,17 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
                       const float* k, const float* v, const float* alpha,
                       float beta, float* o, uint64_t step, float* pre,
                       double* xval) {
-  const int dk = c->dk, dv = c->dv, G = c->G, ng = dk / G;
+  const int dk = c->dk, dv = c->dv;
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
-  std::vector<float> d(dk), sp(dk), stored(dk);
+  std::vector<float> d(dk), Sp((size_t)dv * dk), stored((size_t)dv * dk);
   for (int i = 0; i < dv; ++i) {
+    float* sp = Sp.data() + (size_t)i * dk;
     // dequantize and decay
     for (int j = 0; j < dk; ++j) {
-      const float code = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j);
-      const float s = scales[(size_t)i * ng + j / G];
-      stored[j] = code * s;
+      const int64_t x = (int64_t)i * dk + j;
+      const float code = (float)oracle_get_code(codes, bits, x);
+      const float s = scales[scale_index(c, i, j)];
+      stored[x] = code * s;
       if (vector_decay(c->mixer))
         d[j] = (code * s) * alpha[j];
       else
@@ -289,10 +328,10 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
     }
     // rank-1 write
     for (int j = 0; j < dk; ++j) sp[j] = std::fma(w, k[j], d[j]);
-    if (o) o[i] = oracle_dot(sp.data(), q, dk);
-    if (pre) std::memcpy(pre + (size_t)i * dk, sp.data(), sizeof(float) * dk);
-    quantize_row(c, bits, key, i, sp.data(), stored.data(), codes, scales, xval);
+    if (o) o[i] = oracle_dot(sp, q, dk);
   }
+  if (pre) std::memcpy(pre, Sp.data(), sizeof(float) * Sp.size());
+  quantize_head(c, bits, key, Sp.data(), stored.data(), codes, scales, xval);
 }
 
 // The same step on an unquantized FP32 state (the "FP32 states" the pages
@@ -324,17 +363,16 @@ void oracle_head_quantize(const oracle_cfg* c, int b, int h, int bits,
                           const float* S, uint8_t* codes, float* scales,
                           uint64_t step, double* xval) {
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
-  for (int i = 0; i < c->dv; ++i)
-    quantize_row(c, bits, key, i, S + (size_t)i * c->dk, nullptr, codes, scales, xval);
+  quantize_head(c, bits, key, S, nullptr, codes, scales, xval);
 }
 
 void oracle_head_dequantize(const oracle_cfg* c, int bits, const uint8_t* codes,
                             const float* scales, float* S) {
-  const int dk = c->dk, G = c->G, ng = dk / G;
+  const int dk = c->dk;
   for (int i = 0; i < c->dv; ++i)
     for (int j = 0; j < dk; ++j)
       S[(size_t)i * dk + j] = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j) *
-                              scales[(size_t)i * ng + j / G];
+                              scales[scale_index(c, i, j)];
 }
 
 void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
@@ -351,13 +389,13 @@ void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
 void oracle_step(const oracle_cfg* c, const uint8_t* head_bits, uint8_t* codes,
                  float* scales, const float* q, const float* k, const float* v,
                  const float* alpha, const float* beta, float* o, uint64_t step) {
-  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  const int dk = c->dk, dv = c->dv;
   const int na = vector_decay(c->mixer) ? dk : 1;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
       oracle_head_step(c, b, h, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
-                       scales + bh * dv * ng, q + bh * dk, k + bh * dk, v + bh * dv,
+                       scales + bh * head_scales(c), q + bh * dk, k + bh * dk, v + bh * dv,
                        alpha + bh * na, (c->mixer == kMixerGLA) ? 0.0f : beta[bh],
                        o ? o + bh * dv : nullptr, step, nullptr, nullptr);
     }
@@ -378,35 +416,35 @@ void oracle_step_fp32(const oracle_cfg* c, float* S, const float* q, const float
 
 void oracle_quantize(const oracle_cfg* c, const uint8_t* head_bits, const float* S,
                      uint8_t* codes, float* scales, uint64_t step) {
-  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  const int dk = c->dk, dv = c->dv;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
       oracle_head_quantize(c, b, h, head_bits[h], S + bh * dv * dk,
                            codes + oracle_head_offset(c, head_bits, b, h),
-                           scales + bh * dv * ng, step, nullptr);
+                           scales + bh * head_scales(c), step, nullptr);
     }
 }
 
 void oracle_dequantize(const oracle_cfg* c, const uint8_t* head_bits,
                        const uint8_t* codes, const float* scales, float* S) {
-  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  const int dk = c->dk, dv = c->dv;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
       oracle_head_dequantize(c, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
-                             scales + bh * dv * ng, S + bh * dv * dk);
+                             scales + bh * head_scales(c), S + bh * dv * dk);
     }
 }
 
 void oracle_readout(const oracle_cfg* c, const uint8_t* head_bits, const uint8_t* codes,
                     const float* scales, const float* q, float* o) {
-  const int dk = c->dk, dv = c->dv, ng = dk / c->G;
+  const int dk = c->dk, dv = c->dv;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
       oracle_head_readout(c, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
-                          scales + bh * dv * ng, q + bh * dk, o + bh * dv);
+                          scales + bh * head_scales(c), q + bh * dk, o + bh * dv);
     }
 }
 

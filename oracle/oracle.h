@@ -37,6 +37,9 @@ typedef struct {
                        2 bounded directional (nearest for an import)     */
   uint64_t seed;
   uint32_t layer;
+  int32_t axis;     /* 0 value-axis groups (G key columns of one row, scales
+                       [dv][dk/G]); 1 key-axis groups (G value rows of one
+                       column, scales [dv/G][dk])                       */
 } oracle_cfg;
 
 /* ---- counter-based random bits ---- */
