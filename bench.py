@@ -70,7 +70,7 @@ def algorithmic_bytes(w, hb) -> int:
     once, q, k, v, o, and the gates (alpha per head or per key channel, beta)."""
     per_b = 0
     for h in range(w.H):
-        state = w.dv * w.dk * int(hb[h]) // 8 + w.dv * (w.dk // w.G) * 4
+        state = w.dv * w.dk * int(hb[h]) // 8 + w.dv * w.dk // w.G * 4
         io = 4 * (2 * w.dk + 2 * w.dv)
         per_b += 2 * state + io + gate_bytes(w)
     return per_b * w.B
@@ -87,7 +87,7 @@ def cpu_baseline(w, hb, seconds: float):
     import workloads as W
 
     rng = np.random.default_rng(0)
-    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0)
+    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0, w.axis)
     q, k, v, alpha, beta = W.step_inputs(w, 0)
     heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096), rng.integers(0, w.H, 4096))]
     S0 = rng.standard_normal((w.dv, w.dk)).astype(np.float32)
@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--rounding", type=int, default=None, help="override: 0 RTN, 1 SR, 2 BDR")
+    ap.add_argument("--axis", type=int, default=0,
+                    help="scale groups: 0 value axis (default), 1 key axis")
     ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
     ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -146,12 +148,14 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.rounding is not None:
         w = w.scaled(rounding=args.rounding)
+    w = w.scaled(axis=args.axis)
     policy = {"alpha_gt_0.99": (0, 0.99), "rank_half": (1, 0.5)}.get(w.bits_policy)
     hb = (Q.qstate_bits_by_decay(W.head_retention(w), *policy) if policy
           else np.full(w.H, 8, np.uint8))
     nbytes = algorithmic_bytes(w, hb)
 
-    cfg0 = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0, 0)
+    cfg0 = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0, 0,
+                    w.axis)
     cb, sb = Q.qstate_state_bytes(cfg0)
     n_states = args.states or max(2, int(np.ceil(1.0 * 2**30 / (cb + sb))))
 
@@ -171,7 +175,7 @@ def main():
     states = []
     for layer in range(n_states):
         cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0,
-                       layer)
+                       layer, w.axis)
         s = Q.QState(cfg)
         s.load_fp32(S)
         states.append(s)
@@ -212,7 +216,8 @@ def main():
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "group": w.G,
             "state_bits": {str(b): int((hb == b).sum()) for b in sorted(set(hb.tolist()))},
-            "rounding": ROUNDING_NAMES[w.rounding], "state_instances": n_states,
+            "rounding": ROUNDING_NAMES[w.rounding],
+            "group_axis": "key" if w.axis else "value", "state_instances": n_states,
             "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,
         },
         "hbm_gbps": gbps,

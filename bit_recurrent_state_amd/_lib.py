@@ -20,6 +20,7 @@ QSTATE_E_NOMEM = -4
 
 GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR, BDR = 0, 1, 2
+VALUE_AXIS, KEY_AXIS = 0, 1
 
 EXPORTS = (
     "qstate_state_bytes", "qstate_create", "qstate_load_fp32", "qstate_step",
@@ -34,7 +35,7 @@ class QStateConfig(ctypes.Structure):
         ("dv", ctypes.c_int32), ("group", ctypes.c_int32), ("mixer", ctypes.c_int32),
         ("rounding", ctypes.c_int32), ("fp32_state", ctypes.c_int32),
         ("head_bits", ctypes.POINTER(ctypes.c_uint8)), ("seed", ctypes.c_uint64),
-        ("layer", ctypes.c_uint32),
+        ("layer", ctypes.c_uint32), ("group_axis", ctypes.c_int32),
     ]
 
 

@@ -41,7 +41,11 @@ int check_config(const qstate_config* c) {
   if (c->fp32_state != 0 && c->fp32_state != 1) return QSTATE_E_INVALID;
   if (!c->fp32_state) {
     if (c->rounding < QSTATE_RTN || c->rounding > QSTATE_BDR) return QSTATE_E_INVALID;
-    if (c->group < 1 || c->dk % c->group != 0) return QSTATE_E_INVALID;
+    if (c->group_axis != QSTATE_VALUE_AXIS && c->group_axis != QSTATE_KEY_AXIS)
+      return QSTATE_E_INVALID;
+    // value-axis groups split a row's dk columns, key-axis groups a column's dv rows
+    const int grouped = c->group_axis == QSTATE_KEY_AXIS ? c->dv : c->dk;
+    if (c->group < 1 || grouped % c->group != 0) return QSTATE_E_INVALID;
     if (c->head_bits)
       for (int h = 0; h < c->heads && h < kMaxHeads; ++h)
         if (c->head_bits[h] != 4 && c->head_bits[h] != 8) return QSTATE_E_INVALID;
@@ -71,7 +75,10 @@ void layout(const qstate_config* c, size_t* codes_bytes, size_t* scales_bytes, u
     pb += (uint64_t)c->dv * c->dk * bits / 8;
   }
   *codes_bytes = (size_t)pb * c->batch;
-  *scales_bytes = bh * c->dv * (c->dk / c->group) * sizeof(float);
+  const size_t per_head = c->group_axis == QSTATE_KEY_AXIS
+                              ? (size_t)(c->dv / c->group) * c->dk
+                              : (size_t)c->dv * (c->dk / c->group);
+  *scales_bytes = bh * per_head * sizeof(float);
   if (per_b) *per_b = pb;
 }
 
@@ -84,14 +91,24 @@ qs::KParams base_params(const qstate* s) {
   p.H = s->cfg.heads;
   p.dv = s->cfg.dv;
   p.G = s->cfg.fp32_state ? 16 : s->cfg.group;
-  // One wave per row slice: split heads until the launch has at least
-  // kTargetWaves waves (16 per CU on 256 CUs), in slices of whole 32-row units.
+  p.axis = s->cfg.fp32_state ? 0 : s->cfg.group_axis;
+  // Split heads into row slices until the launch has at least kTargetWaves
+  // waves (16 per CU on 256 CUs).  Value axis: one wave per slice, slices of
+  // whole 32-row units.  Key axis: workgroups of max(1, G / rb) waves, each
+  // owning whole blocks of max(G, rb) rows, rb = 4096 / dk rows per wave.
   const int64_t heads = (int64_t)s->cfg.batch * s->cfg.heads;
-  const int units = (s->cfg.dv + 31) / 32;
-  int slices = (int)std::min<int64_t>((kTargetWaves + heads - 1) / heads, units);
+  int unit_rows = 32, waves_per_slice = 1;
+  if (p.axis == QSTATE_KEY_AXIS) {
+    const int rb = 4096 / s->cfg.dk;
+    unit_rows = std::max(p.G, rb);
+    waves_per_slice = std::max(1, p.G / rb);
+  }
+  const int units = (s->cfg.dv + unit_rows - 1) / unit_rows;
+  const int64_t want = (kTargetWaves + heads * waves_per_slice - 1) / (heads * waves_per_slice);
+  int slices = (int)std::min<int64_t>(want, units);
   slices = std::max(slices, 1);
   const int units_per_slice = (units + slices - 1) / slices;
-  p.slice_rows = 32 * units_per_slice;
+  p.slice_rows = unit_rows * units_per_slice;
   p.slices = (units + units_per_slice - 1) / units_per_slice;
   p.bytes_per_b = s->bytes_per_b;
   p.head_bytes4 = (uint32_t)((uint64_t)s->cfg.dv * s->cfg.dk / 2);

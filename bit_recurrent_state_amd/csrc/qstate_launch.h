@@ -11,18 +11,20 @@ namespace qs {
 // Everything a kernel needs for one launch, passed by value.
 struct KParams {
   void* state;           // codes (quantized) or float S (FP32 state)
-  float* scales;         // [B][H][dv][dk/G]
+  float* scales;         // [B][H][dv][dk/G] (value axis) or [B][H][dv/G][dk] (key axis)
   const float* q;        // [B][H][dk]
   const float* k;        // [B][H][dk]
   const float* v;        // [B][H][dv]
-  const float* alpha;    // [B][H] or [B][H][dk] (GLA)
-  const float* beta;     // [B][H] (GDN, scalar) or null
+  const float* alpha;    // [B][H] or [B][H][dk] (GLA, KDA)
+  const float* beta;     // [B][H] (GDN, scalar, KDA) or null
   float* o;              // [B][H][dv] or null
   const float* src;      // import: FP32 state to quantize
   float* dst;            // export: dequantized FP32 state
   int32_t B, H, dv, G;
-  int32_t slices;        // waves per head (row slices); the grid is B*H*slices
-  int32_t slice_rows;    // rows per slice, a multiple of 32
+  int32_t axis;          // scale groups: 0 value axis, 1 key axis
+  int32_t slices;        // workgroups per head (row slices); the grid is B*H*slices
+  int32_t slice_rows;    // rows per slice: a multiple of 32 (value axis) or of
+                         // the key-axis block rows max(G, 4096/dk)
   uint64_t bytes_per_b;  // code bytes of one batch row (all heads)
   uint32_t head_bytes4;  // code bytes of an INT4 head = dv*dk/2
   uint32_t int8_mask[8]; // bit h set: head h stores INT8 codes

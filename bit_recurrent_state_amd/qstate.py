@@ -13,10 +13,12 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import BDR, GDN, GLA, KDA, RTN, SCALAR, SR, QStateConfig, check, lib
+from ._lib import (BDR, GDN, GLA, KDA, KEY_AXIS, RTN, SCALAR, SR, VALUE_AXIS, QStateConfig, check,
+                   lib)
 
 __all__ = [
-    "GDN", "GLA", "SCALAR", "KDA", "RTN", "SR", "BDR", "Config", "QState",
+    "GDN", "GLA", "SCALAR", "KDA", "RTN", "SR", "BDR", "VALUE_AXIS", "KEY_AXIS", "Config",
+    "QState",
     "qstate_state_bytes", "qstate_create", "qstate_load_fp32", "qstate_step",
     "qstate_readout", "qstate_store_fp32", "qstate_get_step", "qstate_set_step",
     "qstate_destroy", "qstate_bits_by_decay",
@@ -36,6 +38,7 @@ class Config:
     head_bits: Optional[Sequence[int]] = None
     seed: int = 0
     layer: int = 0
+    group_axis: int = VALUE_AXIS
 
     def to_c(self):
         """(QStateConfig, keep-alive buffer)."""
@@ -45,7 +48,8 @@ class Config:
             hb = (ctypes.c_uint8 * self.heads)(*[int(x) for x in self.head_bits])
             ptr = ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8))
         c = QStateConfig(self.batch, self.heads, self.dk, self.dv, self.group, self.mixer,
-                         self.rounding, int(bool(self.fp32_state)), ptr, self.seed, self.layer)
+                         self.rounding, int(bool(self.fp32_state)), ptr, self.seed, self.layer,
+                         self.group_axis)
         return c, hb
 
     def bits(self) -> np.ndarray:

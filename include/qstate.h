@@ -27,7 +27,9 @@
  * is one IEEE-754 binary32 operation with round-to-nearest-even unless noted):
  *
  *  Per head (b,h) with bit width n (4 or 8), r = 2^(n-1) - 1, and per value
- *  row i (0 <= i < dv), key column j (0 <= j < dk), group g = j / G:
+ *  row i (0 <= i < dv), key column j (0 <= j < dk), the element's scale
+ *  group is (i, g = j / G) for value-axis groups and (g = i / G, j) for
+ *  key-axis groups; s_ig below stands for that group's scale:
  *   1. decayed dequantized row
  *        GDN, SCALAR: d_j = c_ij * (s_ig * alpha)
  *        GLA, KDA:    d_j = (c_ij * s_ig) * alpha_j
@@ -42,7 +44,7 @@
  *      KDA S' = S diag(alpha) (I - beta k k^T) + beta v k^T (LoReS blog,
  *      Table 1 "KDA"; vector gates of Prop. "decaying error").
  *   4. o_i = dot(S'_i, q)       (from the full-precision S', before requant)
- *   5. m = max_{j in g} |S'_ij|;  m == 0: s' = 0, inv = 0, codes 0;
+ *   5. m = max over the group of |S'|;  m == 0: s' = 0, inv = 0, codes 0;
  *      else s' = m / r (correctly rounded), inv = the largest float with
  *      inv * m <= r (r / m rounded toward zero), so |S' * inv| <= r.
  *   6. RTN: code = round-half-even(S'_ij * inv)   (exact product)
@@ -82,7 +84,8 @@
  *                   Row-major [dv][dk] inside a head.  INT8: int8 two's
  *                   complement.  INT4: two's-complement nibbles, byte
  *                   (i*dk + j)/2 holds even j in bits 0..3, odd j in 4..7.
- *   scales          float [B][H][dv][dk/G]
+ *   scales          float [B][H][dv][dk/G] (value axis) or [B][H][dv/G][dk]
+ *                   (key axis)
  *   FP32 state      float [B][H][dv][dk]  (fp32_state = 1)
  *
  * Range: state magnitudes stay below 2^120 (far beyond any FP32 recurrence
@@ -123,6 +126,13 @@ typedef enum {
   QSTATE_KDA = 3     /* S' = S diag(alpha[dk]) (I - b k k^T) + b v k^T      */
 } qstate_mixer;
 
+/* Shape of a scale group (LoReS blog, "Scale grouping"). */
+typedef enum {
+  QSTATE_VALUE_AXIS = 0, /* G key columns of one value row: scales [dv][dk/G]
+                            (the default: one output channel per group)     */
+  QSTATE_KEY_AXIS = 1    /* G value rows of one key column: scales [dv/G][dk] */
+} qstate_group_axis;
+
 typedef enum {
   QSTATE_RTN = 0, /* round to nearest, ties to even                        */
   QSTATE_SR = 1,  /* stochastic rounding (counter-based bits)              */
@@ -134,7 +144,8 @@ typedef struct {
   int32_t heads;            /* H, 1..256                                      */
   int32_t dk;               /* key dim (columns): 64, 128 or 256              */
   int32_t dv;               /* value dim (rows): 1..4096                      */
-  int32_t group;            /* G: 16, 32, 64 or 128, divides dk               */
+  int32_t group;            /* G: 16, 32, 64 or 128; divides dk (value axis)
+                               or dv (key axis)                               */
   int32_t mixer;            /* qstate_mixer                                   */
   int32_t rounding;         /* qstate_rounding                                */
   int32_t fp32_state;       /* 1: unquantized FP32 state (baseline); the
@@ -143,6 +154,7 @@ typedef struct {
                                NULL = all 8                                   */
   uint64_t seed;            /* stochastic-rounding key                        */
   uint32_t layer;           /* stochastic-rounding key                        */
+  int32_t group_axis;       /* qstate_group_axis; 0 = value axis (default)    */
 } qstate_config;
 
 typedef struct qstate qstate; /* opaque; host-side metadata only */

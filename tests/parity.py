@@ -97,8 +97,9 @@ class Run:
         else:
             self.hb = head_bits(w, seed, layer)
         self.cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, False,
-                            [int(x) for x in self.hb], seed, layer)
-        self.ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, seed, layer)
+                            [int(x) for x in self.hb], seed, layer, w.axis)
+        self.ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, seed, layer,
+                               w.axis)
         all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
         self.heads = all_heads if heads is None else list(heads)
         self.rep = Report()
@@ -185,7 +186,7 @@ class Run:
     def compare(self, step, o_gpu, o_ref, xvals=None):
         w = self.w
         codes_g = _to_np(self.gpu.codes)
-        scales_g = _to_np(self.gpu.scales).reshape(w.B, w.H, w.dv, w.dk // w.G)
+        scales_g = _to_np(self.gpu.scales).reshape(w.B, w.H, -1)
         for (b, h) in self.heads:
             bits = int(self.hb[h])
             off, n = self.head_codes_slice(b, h)

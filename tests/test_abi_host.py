@@ -59,13 +59,19 @@ def test_state_bytes(L):
     c = _cfg(fp32_state=1)
     assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
     assert cb.value == 2 * 3 * 64 * 128 * 4 and sb.value == 0
+    # key-axis groups: G value rows per scale, [dv/G][dk] scales per head
+    c = _cfg(head_bits=hb, group_axis=1, dk=64, dv=128, group=128)
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 2 * 128 * 64 * (4 + 8 + 4) // 8
+    assert sb.value == 2 * 3 * (128 // 128) * 64 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), -1), (dict(heads=0), -1), (dict(dv=0), -1), (dict(mixer=4), -1),
     (dict(rounding=3), -1), (dict(group=48), -1), (dict(fp32_state=2), -1),
     (dict(dk=96, group=32), -2), (dict(dk=512, group=64), -2), (dict(heads=300), -2),
-    (dict(dv=5000), -2), (dict(group=8), -2),
+    (dict(dv=5000), -2), (dict(group=8), -2), (dict(group_axis=2), -1),
+    (dict(group_axis=1, dv=48, group=32), -1), (dict(group_axis=1, dv=64, group=48), -1),
 ])
 def test_invalid_configs_rejected(L, kw, status):
     c = _cfg(**kw)

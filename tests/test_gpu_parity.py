@@ -24,7 +24,7 @@ else:  # keep collection working on CPU-only hosts
 
 def _run(w, steps, rounding=None, heads=None, seed=0, layer=0, hb=None):
     r = Run(w, rounding, seed, layer, heads, head_bits_override=hb)
-    log(f"[case] {w.name} B={w.B} H={w.H} dk={w.dk} dv={w.dv} G={w.G} mixer={w.mixer} "
+    log(f"[case] {w.name} B={w.B} H={w.H} dk={w.dk} dv={w.dv} G={w.G} axis={w.axis} mixer={w.mixer} "
         f"rounding={r.rounding} bits={sorted(set(r.hb.tolist()))} warmup={w.warmup} "
         f"steps={steps} heads={len(r.heads)} seed={seed} layer={layer}")
     r.warmup_and_import()
@@ -75,6 +75,42 @@ def test_bdr_full_size_sampled_heads():
     rng = np.random.default_rng(12)
     idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
     _run(w, 2, rounding=W.BDR, heads=sorted((i // w.H, i % w.H) for i in idx))
+
+
+KEY_AXIS_RUNS = [(2, W.SR), (3, W.RTN), (3, W.BDR), (4, W.SR), (5, W.SR), (1, W.BDR)]
+
+
+@pytest.mark.parametrize("wid,rounding", KEY_AXIS_RUNS)
+def test_key_axis_every_head(wid, rounding):
+    """Key-axis scale groups (G value rows of one key column) on every
+    recurrence and rounding, mixed bits included."""
+    _run(W.WORKLOADS[wid].scaled(B=2, axis=1), 8, rounding=rounding)
+
+
+# key-axis block shapes: several groups per wave, one group over 2, 4 and 8
+# waves, groups longer than dk, ragged dv (a partial last block)
+KEY_RAGGED = [
+    (W.GDN, W.SR, 64, 48, 16, [8, 4, 4]),
+    (W.GLA, W.RTN, 128, 80, 16, [4, 8]),
+    (W.KDA, W.BDR, 128, 128, 128, [8, 4]),
+    (W.SCALAR, W.SR, 64, 128, 128, [4, 8]),
+    (W.GDN, W.RTN, 256, 256, 128, [8]),
+    (W.GDN, W.BDR, 256, 96, 32, [4, 8]),
+]
+
+
+@pytest.mark.parametrize("mixer,rounding,dk,dv,G,bits", KEY_RAGGED)
+def test_key_axis_shapes(mixer, rounding, dk, dv, G, bits):
+    w = W.Workload(85 + mixer, f"key_m{mixer}_dk{dk}_dv{dv}_g{G}", mixer, 3, len(bits), dk, dv, G,
+                   5, 3, rounding, "int8", axis=1)
+    _run(w, 5, hb=np.array(bits, np.uint8), seed=11)
+
+
+def test_key_axis_full_size_sampled_heads():
+    w = W.WORKLOADS[2].scaled(axis=1)
+    rng = np.random.default_rng(21)
+    idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
+    _run(w, 2, heads=sorted((i // w.H, i % w.H) for i in idx))
 
 
 @pytest.mark.parametrize("layer", [0, 5])

@@ -46,6 +46,7 @@ class Workload:
     rounding: int
     bits_policy: str     # "int8" | "alpha_gt_0.99" | "rank_half"
     layers: int = 1
+    axis: int = 0        # scale groups: 0 value axis (G key columns), 1 key axis (G value rows)
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
