@@ -34,24 +34,34 @@ METRIC = "quantized-state decode steps/s and HBM GB/s (% of peak) at B=256, INT8
 HBM_PEAK_GBPS = 8000.0
 ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", "qstate_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", f)
+               for f in ("qstate_device.h", "qstate_value.h", "qstate_key.h")]
 
 
 def kernel_source_hash() -> str:
+    """sha256[:16] of the decode kernels' source (all scale-group layouts)."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
+def traffic_key(w) -> str:
+    return f"{w.name}|{ROUNDING_NAMES[w.rounding]}|{'key' if w.axis else 'value'}-axis"
+
+
+def measured_traffic(w):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counts (scaled by the same counters on a copy of known size); None when the
-    kernel source changed since they were taken."""
+    counts of this workload, rounding and group axis (scaled by the same
+    counters on an in-place xor of known size); None when they were not taken
+    or the kernel source changed since."""
     try:
         import json as _j
         t = _j.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get("workloads", {}).get(workload_name)
+    e = t.get("workloads", {}).get(traffic_key(w))
     if not e or t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return e["hbm_bytes_per_launch"]
@@ -223,7 +233,7 @@ def main():
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name),
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w),
                      "algorithmic_bytes_per_launch": nbytes},
     }
 

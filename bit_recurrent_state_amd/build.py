@@ -1,8 +1,10 @@
 """Compile libqstate.so (gfx950) in-tree with hipcc.
 
-Flags: no FP contraction (every fused multiply-add in the kernels is an
-explicit fmaf), IEEE-correct FP32 division, FP32 denormals kept, and packed
-FP32 instructions switched off.
+Each kernel source (one per dk and scale-group axis) and the host sources
+compile to objects in parallel under _build/, then link into the shared
+library.  Flags: no FP contraction (every fused multiply-add in the kernels
+is an explicit fmaf), IEEE-correct FP32 division, FP32 denormals kept, and
+packed FP32 instructions switched off.
 """
 
 from __future__ import annotations
@@ -15,12 +17,17 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqstate.so")
-SOURCES = [os.path.join(CSRC, "qstate_kernels.hip"), os.path.join(CSRC, "qstate_api.cpp")]
-HEADERS = [os.path.join(ROOT, "include", "qstate.h"), os.path.join(CSRC, "qstate_launch.h")]
+SOURCES = ([os.path.join(CSRC, f"qstate_{axis}_dk{dk}.hip")
+            for axis in ("value", "key") for dk in (64, 128, 256)]
+           + [os.path.join(CSRC, "qstate_dispatch.cpp"), os.path.join(CSRC, "qstate_api.cpp")])
+HEADERS = [os.path.join(ROOT, "include", "qstate.h")] + [
+    os.path.join(CSRC, h) for h in ("qstate_launch.h", "qstate_device.h", "qstate_value.h",
+                                    "qstate_key.h")]
+BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,14 +35,30 @@ FLAGS = [
 ]
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out,
-            *SOURCES]
+def compile_command(src: str, obj: str, extra=()) -> list:
+    return [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+            "-o", obj, src]
 
 
-def build(out: str = LIB, extra=()) -> str:
+def build(out: str = LIB, extra=(), jobs: int = 0) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in SOURCES]
+    pending = list(zip(SOURCES, objs))
+    running = []
+    failed = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            src, obj = pending.pop(0)
+            running.append((src, subprocess.Popen(compile_command(src, obj, extra))))
+        src, proc = running.pop(0)
+        if proc.wait() != 0:
+            failed.append(src)
+    if failed:
+        raise subprocess.CalledProcessError(1, f"hipcc: {', '.join(failed)}")
     tmp = out + ".tmp"
-    subprocess.run(command(tmp, extra), check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                   check=True)
     os.replace(tmp, out)
     return out
 

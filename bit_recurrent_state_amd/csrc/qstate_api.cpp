@@ -1,6 +1,7 @@
 // qstate_api.cpp — the C ABI declared in include/qstate.h: argument checks,
 // the host-side handle, per-head layout and kernel dispatch.  Host code only;
-// every byte of the step is computed by the kernels in qstate_kernels.hip.
+// every byte of the step is computed by the kernels in qstate_value_dk*.hip
+// and qstate_key_dk*.hip.
 
 #include "qstate.h"
 

@@ -1,0 +1,396 @@
+// qstate_device.h — device helpers shared by the gfx950 decode kernels:
+// counter-based random bits, DPP row reductions, the fixed-order dot
+// products, group scales, code unpacking/packing and requantization of
+// 16-element chunks, per-head geometry.  Included by each kernel source;
+// everything here has internal linkage.
+//
+// One wave (a workgroup of 64 lanes) owns a slice of the rows of one head
+// (b, h); small batches split a head into several slices so that enough
+// waves exist to fill 256 CUs.  A value row of the state is split across
+// adjacent lanes: each lane owns one 16-byte run of codes, i.e. 16 INT8
+// elements or 32 INT4 elements, so a row of dk columns spans dk/16 (INT8) or
+// dk/32 (INT4) lanes and the wave holds the rest of its 64 lanes as further
+// rows.  The loads of the next kPrefetch row iterations are in flight while
+// the current one is computed.  Every operation of the step is row-local (LoReS
+// blog, "LoReS: State Quantization": value-axis groups, full-precision update,
+// readout from the updated state): the two dot products u = d.k and o = S'.q
+// finish with DPP butterflies across the row's lanes, the group absmax with
+// DPP butterflies across the group's lanes.  No LDS, no atomics, no
+// cross-workgroup traffic: each state byte is read once and written once.
+//
+// Arithmetic follows the semantics written in include/qstate.h operation by
+// operation (explicit fmaf, no contraction, IEEE division), so the stored
+// codes are bit-identical to any other implementation of those semantics.
+// The 16-element chunks and the butterflies realise the summation order
+// defined there: sequential fused multiply-adds inside a chunk, then a
+// pairwise tree over the chunks (an INT4 lane adds its two adjacent chunks,
+// then DPP pairs adjacent lanes, adjacent lane pairs, ...).
+//
+// Instruction economy (the INT4 + stochastic-rounding path is VALU-bound):
+//  * codes are turned into floats with v_cvt_f32_ubyte after flipping the
+//    sign bit of each byte/nibble (offset binary c + 2^(n-1)); the decayed
+//    value c*sa is then one fma(cu, sa, -2^(n-1)*sa), which is exactly the
+//    rounded product c*sa because the addend is exact;
+//  * stochastic rounding evaluates floor(S'*inv + R/2^16) as
+//    floor(fma(S', inv*2^16, R) / 2^16): the scaling by 2^16 is exact, so the
+//    code is byte 2 of floor(fma(...)), gathered with v_perm_b32;
+//  * round-to-nearest adds 1.5*2^23 inside the fma, which leaves the rounded
+//    code in the low byte of the result.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qstate_launch.h"
+
+namespace qs {
+namespace {
+
+constexpr int kThreads = 64;  // one wave per workgroup
+constexpr int kPrefetch = 4;  // row iterations whose loads are in flight ahead of compute
+constexpr int kGDN = 0, kGLA = 1, kScalar = 2, kKDA = 3;
+constexpr int kRTN = 0, kSR = 1, kBDR = 2;  // rounding of the step
+// per-key-channel decay (GLA, KDA) and the delta-rule write weight (GDN, KDA)
+constexpr bool vector_decay(int m) { return m == kGLA || m == kKDA; }
+constexpr bool delta_rule(int m) { return m == kGDN || m == kKDA; }
+
+// ---------------------------------------------------------------------------
+// Counter-based random bits (semantics in include/qstate.h).
+// ---------------------------------------------------------------------------
+
+// SplitMix64 output function (Steele, Lea & Flood 2014).
+__device__ __forceinline__ uint64_t splitmix64_out(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Key of (seed, layer, step, b, h): x = F((x ^ field) + golden) from x = 0.
+__device__ __forceinline__ uint32_t head_key(const KParams& p, uint32_t b, uint32_t h) {
+  constexpr uint64_t golden = 0x9E3779B97F4A7C15ull;
+  uint64_t x = splitmix64_out(p.seed + golden);
+  x = splitmix64_out((x ^ (uint64_t)p.layer) + golden);
+  x = splitmix64_out((x ^ p.step) + golden);
+  x = splitmix64_out((x ^ (uint64_t)b) + golden);
+  x = splitmix64_out((x ^ (uint64_t)h) + golden);
+  return (uint32_t)(x >> 32) ^ (uint32_t)x;
+}
+
+// MurmurHash3 32-bit finalizer (Appleby).
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Marsaglia's xorshift32, shifts 13, 17, 5.
+__device__ __forceinline__ uint32_t xorshift32(uint32_t y) {
+  y ^= y << 13;
+  y ^= y >> 17;
+  y ^= y << 5;
+  return y;
+}
+
+// The 16 random 16-bit values R of one 16-element block, as floats: one
+// hashed seed and a walk of seven xorshift32 steps give the block's eight
+// 32-bit words (low half: even element, high half: odd element).
+__device__ __forceinline__ void block_r16(uint32_t key, uint32_t block, float* r) {
+  uint32_t w = fmix32(key ^ block);
+  w = w > 1u ? w : 1u;
+#pragma unroll
+  for (int pr = 0; pr < 8; ++pr) {
+    if (pr) w = xorshift32(w);
+    r[2 * pr] = (float)(w & 0xFFFFu);
+    r[2 * pr + 1] = (float)(w >> 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DPP butterflies inside a 16-lane row of the wave.  After the two quad
+// levels every lane of a quad holds the quad's value, so the half-row mirror
+// pairs quad 0 with quad 1 and the row mirror pairs the two halves: each
+// level adds adjacent partials of the tree, as xor butterflies would.
+// ---------------------------------------------------------------------------
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int LANES>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (LANES >= 2) x = x + dpp<kDppXor1>(x);
+  if constexpr (LANES >= 4) x = x + dpp<kDppXor2>(x);
+  if constexpr (LANES >= 8) x = x + dpp<kDppHalfMirror>(x);
+  if constexpr (LANES >= 16) x = x + dpp<kDppMirror>(x);
+  return x;
+}
+
+template <int LANES>
+__device__ __forceinline__ float lanes_max(float m) {
+  if constexpr (LANES >= 2) m = fmaxf(m, dpp<kDppXor1>(m));
+  if constexpr (LANES >= 4) m = fmaxf(m, dpp<kDppXor2>(m));
+  if constexpr (LANES >= 8) m = fmaxf(m, dpp<kDppHalfMirror>(m));
+  return m;
+}
+
+// Sequential fused dot product of the 16-element chunk starting at x[off].
+template <int N>
+__device__ __forceinline__ float chunk_dot(const float (&x)[N], const float (&y)[N], int off) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(x[off + j], y[off + j], acc);
+  return acc;
+}
+
+// Lane partial of a row dot product: the lane's chunks summed in order.
+template <int N>
+__device__ __forceinline__ float lane_dot(const float (&x)[N], const float (&y)[N]) {
+  float acc = chunk_dot(x, y, 0);
+  if constexpr (N == 32) acc = acc + chunk_dot(x, y, 16);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Scale of a group: s = m / r; inv = r / m rounded toward zero (the largest
+// float with inv * m <= r); an all-zero group gets s = inv = 0.
+// ---------------------------------------------------------------------------
+
+// s = m / r, correctly rounded, as one product and one fused correction:
+// with c = RN(1/r), q = m*c, e = fma(-q, r, m), fma(e, c, q) equals RN(m/r)
+// for every normal m when r is 7 or 127 (an exhaustive check over all
+// mantissas is part of the tests); tiny m keeps the IEEE division.
+template <int R>
+__device__ __forceinline__ void group_scale(float m, float& s, float& inv) {
+  constexpr float r = (float)R;
+  constexpr float c = 1.0f / (float)R;
+  const float q = m * c;
+  s = __builtin_fmaf(__builtin_fmaf(-q, r, m), c, q);
+  if (__builtin_expect(m < 0x1p-100f && m != 0.0f, 0)) s = m / r;
+  float v = r / m;
+  if (__builtin_fmaf(m, v, -r) > 0.0f) v = __int_as_float(__float_as_int(v) - 1);
+  inv = (m == 0.0f) ? 0.0f : v;
+}
+
+// ---------------------------------------------------------------------------
+// Lane geometry: one 16-byte run of codes per lane.
+// ---------------------------------------------------------------------------
+
+template <int DK, int BITS>
+struct Geo {
+  static constexpr int E = BITS == 4 ? 32 : 16;  // elements per lane
+  static constexpr int LPR = DK / E;             // lanes per row
+  static constexpr int RPW = 64 / LPR;           // rows per wave iteration
+  static constexpr int ROW_BYTES = DK * BITS / 8;
+};
+
+// Codes to floats in offset binary: cu = c + 2^(BITS-1).  16 elements from
+// four words (INT8) or two words (INT4).
+template <int BITS>
+__device__ __forceinline__ void unpack16(const uint32_t* w, float* cu) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t x = w[q] ^ 0x80808080u;
+      asm("" : "+v"(x));  // convert bytes in place (v_cvt_f32_ubyte0..3)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) cu[4 * q + p] = (float)((x >> (8 * p)) & 0xFFu);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t x = w[q] ^ 0x88888888u;
+      uint32_t lo = x & 0x0F0F0F0Fu;         // even elements, one per byte
+      uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // odd elements
+      asm("" : "+v"(lo));  // convert bytes in place (v_cvt_f32_ubyte0..3)
+      asm("" : "+v"(hi));
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        cu[8 * q + 2 * p] = (float)((lo >> (8 * p)) & 0xFFu);
+        cu[8 * q + 2 * p + 1] = (float)((hi >> (8 * p)) & 0xFFu);
+      }
+    }
+  }
+}
+
+// Bytes [a.BP, b.BP, c.BP, d.BP] of four words.
+template <int BP>
+__device__ __forceinline__ uint32_t gather4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  constexpr uint32_t sel = 0x0C0C0000u | ((4u + BP) << 8) | (uint32_t)BP;
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, sel);
+  return lo | (hi << 16);
+}
+
+// Pack 16 codes (byte BP of each word of src): four words (INT8) or two (INT4).
+template <int BITS, int BP>
+__device__ __forceinline__ void pack16(const uint32_t* src, uint32_t* out) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      out[q] = gather4<BP>(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t ev = gather4<BP>(src[8 * q], src[8 * q + 2], src[8 * q + 4], src[8 * q + 6]);
+      const uint32_t od = gather4<BP>(src[8 * q + 1], src[8 * q + 3], src[8 * q + 5], src[8 * q + 7]);
+      out[q] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+    }
+  }
+}
+
+// floor(x) as int32 in one instruction.
+__device__ __forceinline__ int32_t floor_i32(float x) {
+  int32_t r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Requantize one 16-element chunk with inverse scale inv into 16 packed codes
+// (four words for INT8, two for INT4).  block: the chunk's 16-element block
+// index in the head (stochastic rounding).  wprev / s_old: the chunk's codes
+// and scale before the step, s_new its new scale (bounded directional
+// rounding).
+template <int BITS, int RND>
+__device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t key, uint32_t block,
+                                           const uint32_t* wprev, float s_old, float s_new,
+                                           uint32_t* out) {
+  uint32_t src[16];
+  if constexpr (RND == kSR) {
+    float R[16];
+    block_r16(key, block, R);
+    if (__builtin_expect(inv <= 0x1p100f, 1)) {
+      const float i16 = inv * 65536.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], i16, R[j]));
+    } else {  // groups of tiny magnitude, where inv * 2^16 could overflow
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv, R[j] * (1.0f / 65536.0f))) << 16;
+    }
+    pack16<BITS, 2>(src, out);
+  } else {
+    // y = 1.5*2^23 + rint(S'*inv): the code sits in the low mantissa bits.
+    constexpr float kMagic = 12582912.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv, kMagic));
+    if constexpr (RND == kBDR) {
+      // prev = c*s_old exactly as stored; the nearest code's stored value
+      // (y - magic)*s_new; where prev lies strictly between that value and
+      // S', step one code toward S' (y stays in the magic's binade, so +-1
+      // is exact), then clamp to [-r, r].
+      constexpr int R = (1 << (BITS - 1)) - 1;
+      constexpr float bias = (float)(1 << (BITS - 1));
+      float prev[16];
+      unpack16<BITS>(wprev, prev);
+      const float nb = -bias * s_old;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = __builtin_fmaf(prev[j], s_old, nb);
+        float y = __uint_as_float(src[j]);
+        const float st = (y - kMagic) * s_new;
+        const float x = sp[j];
+        if (x > pv && st < pv) y += 1.0f;
+        if (x < pv && st > pv) y -= 1.0f;
+        y = fminf(fmaxf(y, kMagic - (float)R), kMagic + (float)R);
+        src[j] = __float_as_uint(y);
+      }
+    }
+    pack16<BITS, 0>(src, out);
+  }
+}
+
+// Requantize the lane's E elements of the updated row S' into 16 bytes of
+// codes.  LPG = 0: two groups per lane (INT4 with G = 16, one per chunk);
+// otherwise one group spanning LPG lanes.  s0/s1: the scales of the lane's
+// groups (in: before the step, used by bounded directional rounding; out:
+// the new ones).  wprev: the lane's four code words before the step.
+template <int BITS, int RND, int E, int LPG>
+__device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t key, uint32_t block0,
+                                               const uint32_t* wprev, float& s0, float& s1) {
+  constexpr int R = (1 << (BITS - 1)) - 1;
+  const float so0 = s0, so1 = s1;
+  float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m0 = fmaxf(m0, fabsf(sp[j]));
+  if constexpr (E == 32) {
+#pragma unroll
+    for (int j = 16; j < 32; ++j) m1 = fmaxf(m1, fabsf(sp[j]));
+  }
+  float inv0, inv1;
+  if constexpr (LPG == 0) {
+    group_scale<R>(m0, s0, inv0);
+    group_scale<R>(m1, s1, inv1);
+  } else {
+    m0 = lanes_max<LPG>(fmaxf(m0, m1));
+    group_scale<R>(m0, s0, inv0);
+    s1 = s0, inv1 = inv0;
+  }
+  uint32_t o[4];
+  quantize16<BITS, RND>(sp, inv0, key, block0, wprev, so0, s0, o);
+  if constexpr (E == 32)
+    quantize16<BITS, RND>(sp + 16, inv1, key, block0 + 1, wprev + 2, so1, s1, o + 2);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Per-head geometry.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool head_is_int8(const KParams& p, int h) {
+  return (p.int8_mask[h >> 5] >> (h & 31)) & 1u;
+}
+
+// Byte offset of head (b, h): b * bytes_per_b + sum_{h' < h} bytes(h'), an
+// INT8 head being twice an INT4 head.
+__device__ __forceinline__ uint64_t head_code_offset(const KParams& p, int b, int h) {
+  uint32_t n8 = 0;
+  for (int w = 0; w < (h >> 5); ++w) n8 += __popc(p.int8_mask[w]);
+  if (h & 31) n8 += __popc(p.int8_mask[h >> 5] & ((1u << (h & 31)) - 1u));
+  return (uint64_t)b * p.bytes_per_b + (uint64_t)(h + n8) * p.head_bytes4;
+}
+
+template <int N>
+__device__ __forceinline__ void loadv(const float* ptr, float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    const float4 t = reinterpret_cast<const float4*>(ptr)[q];
+    x[4 * q] = t.x, x[4 * q + 1] = t.y, x[4 * q + 2] = t.z, x[4 * q + 3] = t.w;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void storev(float* ptr, const float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q)
+    reinterpret_cast<float4*>(ptr)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+}
+
+// The wave's head and row slice [r0, r1).
+struct Slice {
+  int head, b, h, r0, r1;
+};
+
+__device__ __forceinline__ Slice wave_slice(const KParams& p) {
+  Slice sl;
+  sl.head = blockIdx.x / p.slices;
+  const int part = blockIdx.x - sl.head * p.slices;
+  sl.b = sl.head / p.H;
+  sl.h = sl.head - sl.b * p.H;
+  sl.r0 = part * p.slice_rows;
+  sl.r1 = min(p.dv, sl.r0 + p.slice_rows);
+  return sl;
+}
+
+}  // namespace
+}  // namespace qs

@@ -1,0 +1,388 @@
+// qstate_key.h — key-axis decode kernels (scale groups of G value rows
+// inside one key column), templated on dk.  Each qstate_key_dk*.hip
+// instantiates one dk.
+
+#pragma once
+
+#include "qstate_device.h"
+
+namespace qs {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Key-axis scale groups: G consecutive value rows of one key column share a
+// scale (LoReS blog, "Scale grouping", the comparison to the value-axis
+// default; C_j of Prop. "per-channel readout error").  A group's absmax spans
+// rows held by different lanes and iterations, so a workgroup keeps a block
+// of rows' updated values in registers, combines partial column maxima
+// through LDS, and requantizes once every column's scale is known.  Each lane
+// owns a 16-element run of a row (16 bytes of INT8 or 8 bytes of INT4), so a
+// row spans dk/16 lanes and the dot products use the same butterflies and
+// summation order as the value-axis kernels.  Scales: [B][H][dv/G][dk].
+// ---------------------------------------------------------------------------
+
+template <int DK, int G>
+struct KGeo {
+  static constexpr int E = 16;                    // elements per lane
+  static constexpr int LPR = DK / E;              // lanes per row
+  static constexpr int RPW = 64 / LPR;            // rows per wave iteration
+  static constexpr int NI = 4;                    // iterations a wave holds
+  static constexpr int RB = NI * RPW;             // rows per wave block: 4096 / dk
+  static constexpr int NW = G > RB ? G / RB : 1;  // waves per workgroup
+  static constexpr int BR = NW * RB;              // rows per workgroup block
+  static constexpr int LG = BR / G;               // row groups per block
+  static constexpr int PARTS = NW * RPW;          // partial maxima per column and group
+};
+
+// Requantize 16 elements with one inverse scale per element (key-axis
+// groups).  Same rounding as quantize16; inv16/s_old/s_new per element.
+template <int BITS, int RND>
+__device__ __forceinline__ void quantize16_cols(const float* sp, const float* inv16, uint32_t key,
+                                                uint32_t block, const uint32_t* wprev,
+                                                const float* s_old, const float* s_new,
+                                                uint32_t* out) {
+  uint32_t src[16];
+  if constexpr (RND == kSR) {
+    float R[16];
+    block_r16(key, block, R);
+    float imax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) imax = fmaxf(imax, inv16[j]);
+    if (__builtin_expect(imax <= 0x1p100f, 1)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j] * 65536.0f, R[j]));
+    } else {  // a tiny-magnitude group, where inv * 2^16 could overflow
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j], R[j] * (1.0f / 65536.0f)))
+                 << 16;
+    }
+    pack16<BITS, 2>(src, out);
+  } else {
+    constexpr float kMagic = 12582912.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv16[j], kMagic));
+    if constexpr (RND == kBDR) {
+      constexpr int R = (1 << (BITS - 1)) - 1;
+      constexpr float bias = (float)(1 << (BITS - 1));
+      float prev[16];
+      unpack16<BITS>(wprev, prev);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = __builtin_fmaf(prev[j], s_old[j], -bias * s_old[j]);
+        float y = __uint_as_float(src[j]);
+        const float st = (y - kMagic) * s_new[j];
+        const float x = sp[j];
+        if (x > pv && st < pv) y += 1.0f;
+        if (x < pv && st > pv) y -= 1.0f;
+        y = fminf(fmaxf(y, kMagic - (float)R), kMagic + (float)R);
+        src[j] = __float_as_uint(y);
+      }
+    }
+    pack16<BITS, 0>(src, out);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void lds_load(const float* ptr, float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    const float4 t = reinterpret_cast<const float4*>(ptr)[q];
+    x[4 * q] = t.x, x[4 * q + 1] = t.y, x[4 * q + 2] = t.z, x[4 * q + 3] = t.w;
+  }
+}
+
+// Step (OP = kStep) or import (OP = kImport) of a quantized head with
+// key-axis groups.  LDS: partial column maxima, old scales, new scales and
+// inverse scales of the block's row groups.
+template <int OP, int MIXER, int RND, int DK, int BITS, int G>
+__device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl, float* lds) {
+  using K = KGeo<DK, G>;
+  constexpr int E = K::E, LPR = K::LPR, RPW = K::RPW, NI = K::NI, RB = K::RB, NW = K::NW;
+  constexpr int BR = K::BR, LG = K::LG, PARTS = K::PARTS;
+  constexpr int R = (1 << (BITS - 1)) - 1;
+  constexpr float bias = (float)(1 << (BITS - 1));
+  constexpr int ROW_BYTES = DK * BITS / 8;
+  constexpr int LANE_BYTES = E * BITS / 8;  // 16 (INT8) or 8 (INT4)
+  constexpr int NWORDS = LANE_BYTES / 4;
+  float* pm = lds;                        // [LG][PARTS][DK]
+  float* so = pm + LG * PARTS * DK;       // [LG][DK] scales before the step
+  float* sn = so + LG * DK;               // [LG][DK] new scales
+  float* si = sn + LG * DK;               // [LG][DK] new inverse scales
+
+  const int tid = threadIdx.x;
+  const int wv = tid / 64;
+  const int lane = tid % 64;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * (p.dv / G) * DK;
+  const uint32_t key =
+      (RND == kSR) ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+
+  float kk[E], qq[E], al[E];
+  float alpha_s = 0.0f, beta = 0.0f;
+  const float* vh = nullptr;
+  float* oh = nullptr;
+  if constexpr (OP == kStep) {
+    loadv(p.k + (size_t)sl.head * DK + col0, kk);
+    loadv(p.q + (size_t)sl.head * DK + col0, qq);
+    if constexpr (vector_decay(MIXER)) {
+      loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) al[j] = 0.0f;
+      alpha_s = p.alpha[sl.head];
+    }
+    if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
+    vh = p.v + (size_t)sl.head * p.dv;
+    oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  }
+
+  for (int base = sl.r0; base < sl.r1; base += BR) {
+    // scales of the block's row groups before the step
+    if constexpr (OP == kStep) {
+      for (int t = tid; t < LG * DK; t += 64 * NW) {
+        const int grow = base / G + t / DK;
+        so[t] = grow * G < p.dv ? hscales[(size_t)grow * DK + t % DK] : 0.0f;
+      }
+    }
+    // this wave's rows: base + wv*RB + it*RPW + rsub; every row of an
+    // iteration lies in one row group, and a group is wholly inside dv or
+    // wholly outside (G divides dv, RPW divides G)
+    uint32_t wc[NI][4] = {};
+    float vr[NI] = {};
+    float sp[NI][E];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int row = min(base + wv * RB + it * RPW + rsub, p.dv - 1);
+      if constexpr (OP == kStep) {
+        const uint8_t* src = hcodes + (size_t)row * ROW_BYTES + lr * LANE_BYTES;
+        if constexpr (NWORDS == 4) {
+          const uint4 t = *reinterpret_cast<const uint4*>(src);
+          wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = t.z, wc[it][3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(src);
+          wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = 0u, wc[it][3] = 0u;
+        }
+        vr[it] = vh[row];
+      } else {
+        loadv(p.src + ((size_t)sl.head * p.dv + row) * DK + col0, sp[it]);
+      }
+    }
+    if constexpr (OP == kStep) __syncthreads();  // old scales in LDS
+
+    // update (step) and running column maxima per row group
+    float cm[E];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int lg = (wv * RB + it * RPW) / G;  // constant per it when NW == 1, else 0
+      const bool first = NW > 1 ? it == 0 : (it * RPW) % G == 0;
+      const bool last = NW > 1 ? it == NI - 1 : ((it + 1) * RPW) % G == 0;
+      if constexpr (OP == kStep) {
+        const int row = base + wv * RB + it * RPW + rsub;
+        float sc[E];
+        lds_load(so + lg * DK + col0, sc);
+        float d[E];
+        unpack16<BITS>(wc[it], d);
+        if constexpr (vector_decay(MIXER)) {
+#pragma unroll
+          for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], sc[j], -bias * sc[j]) * al[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < E; ++j) {
+            const float sa = sc[j] * alpha_s;
+            d[j] = __builtin_fmaf(d[j], sa, -bias * sa);
+          }
+        }
+        float wt;
+        if constexpr (delta_rule(MIXER)) {
+          const float u = row_sum<LPR>(lane_dot(d, kk));
+          wt = beta * (vr[it] - u);
+        } else if constexpr (MIXER == kGLA) {
+          wt = vr[it];
+        } else {
+          wt = beta * vr[it];
+        }
+#pragma unroll
+        for (int j = 0; j < E; ++j) sp[it][j] = __builtin_fmaf(wt, kk[j], d[j]);
+        const float o = row_sum<LPR>(lane_dot(sp[it], qq));
+        if (oh && lr == 0 && row < p.dv) oh[row] = o;
+      }
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        cm[j] = first ? fabsf(sp[it][j]) : fmaxf(cm[j], fabsf(sp[it][j]));
+      if (last) {
+        float* dst = pm + ((size_t)lg * PARTS + wv * RPW + rsub) * DK + col0;
+#pragma unroll
+        for (int q4 = 0; q4 < E / 4; ++q4)
+          reinterpret_cast<float4*>(dst)[q4] =
+              make_float4(cm[4 * q4], cm[4 * q4 + 1], cm[4 * q4 + 2], cm[4 * q4 + 3]);
+      }
+    }
+    __syncthreads();  // every partial maximum in LDS
+
+    // one thread per (row group, column): absmax, scale, inverse scale
+    for (int t = tid; t < LG * DK; t += 64 * NW) {
+      const int lg = t / DK, j = t % DK;
+      float m = 0.0f;
+#pragma unroll 8
+      for (int q = 0; q < PARTS; ++q) m = fmaxf(m, pm[((size_t)lg * PARTS + q) * DK + j]);
+      float s, inv;
+      group_scale<R>(m, s, inv);
+      sn[t] = s;
+      si[t] = inv;
+      const int grow = base / G + lg;
+      if (grow * G < p.dv) hscales[(size_t)grow * DK + j] = s;
+    }
+    __syncthreads();  // new scales in LDS
+
+    // requantize and store
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int lg = (wv * RB + it * RPW) / G;
+      const int row = base + wv * RB + it * RPW + rsub;
+      float inv16[E], s_old[E], s_new[E];
+      lds_load(si + lg * DK + col0, inv16);
+      if constexpr (RND == kBDR) {
+        lds_load(so + lg * DK + col0, s_old);
+        lds_load(sn + lg * DK + col0, s_new);
+      }
+      uint32_t out[4];
+      const uint32_t block = (uint32_t)((row * DK + col0) >> 4);
+      quantize16_cols<BITS, (OP == kImport && RND == kBDR) ? kRTN : RND>(
+          sp[it], inv16, key, block, wc[it], s_old, s_new, out);
+      if (row < p.dv) {
+        uint8_t* dst = hcodes + (size_t)row * ROW_BYTES + lr * LANE_BYTES;
+        if constexpr (NWORDS == 4)
+          *reinterpret_cast<uint4*>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
+        else
+          *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+      }
+    }
+    __syncthreads();  // LDS free for the next block
+  }
+}
+
+// Export (dequantize) or readout of a quantized head with key-axis groups.
+template <int OP, int DK, int BITS, int G>
+__device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
+  using K = KGeo<DK, G>;
+  constexpr int E = K::E, LPR = K::LPR, RPW = K::RPW, NW = K::NW;
+  constexpr float bias = (float)(1 << (BITS - 1));
+  constexpr int ROW_BYTES = DK * BITS / 8;
+  constexpr int LANE_BYTES = E * BITS / 8;
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int lr = lane % LPR;
+  const int col0 = lr * E;
+  const uint8_t* hcodes =
+      reinterpret_cast<const uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  const float* hscales = p.scales + (size_t)sl.head * (p.dv / G) * DK;
+  float qq[E];
+  if constexpr (OP == kReadout) loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  // the workgroup's NW waves take consecutive row iterations
+  for (int rbase = sl.r0 + (tid / 64) * RPW; rbase < sl.r1; rbase += NW * RPW) {
+    const int row = rbase + lane / LPR;
+    const bool ok = row < sl.r1;
+    const int rr = min(row, p.dv - 1);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    const uint8_t* src = hcodes + (size_t)rr * ROW_BYTES + lr * LANE_BYTES;
+    if constexpr (LANE_BYTES == 16) {
+      const uint4 t = *reinterpret_cast<const uint4*>(src);
+      w[0] = t.x, w[1] = t.y, w[2] = t.z, w[3] = t.w;
+    } else {
+      const uint2 t = *reinterpret_cast<const uint2*>(src);
+      w[0] = t.x, w[1] = t.y;
+    }
+    float sc[E], d[E];
+    loadv(hscales + (size_t)(rr / G) * DK + col0, sc);
+    unpack16<BITS>(w, d);
+#pragma unroll
+    for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], sc[j], -bias * sc[j]);
+    if constexpr (OP == kExport) {
+      if (ok) storev(p.dst + ((size_t)sl.head * p.dv + row) * DK + col0, d);
+    } else {
+      const float o = row_sum<LPR>(lane_dot(d, qq));
+      if (ok && lr == 0) p.o[(size_t)sl.head * p.dv + row] = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels and dispatch.
+// ---------------------------------------------------------------------------
+
+template <int OP, int MIXER, int RND, int DK, int G>
+__global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_kernel(const KParams p) {
+  using K = KGeo<DK, G>;
+  __shared__ float lds[K::LG * (K::PARTS + 3) * DK];
+  const Slice sl = wave_slice(p);
+  if (head_is_int8(p, sl.h))
+    key_quant_head<OP, MIXER, RND, DK, 8, G>(p, sl, lds);
+  else
+    key_quant_head<OP, MIXER, RND, DK, 4, G>(p, sl, lds);
+}
+
+template <int OP, int DK, int G>
+__global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_aux_kernel(const KParams p) {
+  const Slice sl = wave_slice(p);
+  if (head_is_int8(p, sl.h))
+    key_aux_head<OP, DK, 8, G>(p, sl);
+  else
+    key_aux_head<OP, DK, 4, G>(p, sl);
+}
+
+// FP32-state readout: o = S q.
+template <int DK, int G>
+hipError_t launch_key(Op op, int mixer, int rnd, const KParams& p, hipStream_t s) {
+  using K = KGeo<DK, G>;
+  if (p.slice_rows % K::BR != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.B * p.H * p.slices)), block(64 * K::NW);
+  switch (op) {
+    case kStep:
+#define QS_KSTEP(M)                                                                  \
+  if (mixer == M) {                                                                  \
+    switch (rnd) {                                                                   \
+      case kRTN: key_kernel<kStep, M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
+      case kSR: key_kernel<kStep, M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
+      case kBDR: key_kernel<kStep, M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
+      default: return hipErrorInvalidValue;                                          \
+    }                                                                                \
+    return hipGetLastError();                                                        \
+  }
+      QS_KSTEP(kGDN) QS_KSTEP(kGLA) QS_KSTEP(kScalar) QS_KSTEP(kKDA)
+#undef QS_KSTEP
+      return hipErrorInvalidValue;
+    case kImport:  // nothing stored before an import: BDR rounds to nearest
+      if (rnd == kSR)
+        key_kernel<kImport, kGDN, kSR, DK, G><<<grid, block, 0, s>>>(p);
+      else
+        key_kernel<kImport, kGDN, kRTN, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    case kExport:
+      key_aux_kernel<kExport, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    case kReadout:
+      key_aux_kernel<kReadout, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <int DK>
+hipError_t launch_key_dk(Op op, int mixer, int rnd, const KParams& p, hipStream_t s) {
+  switch (p.G) {
+    case 16: return launch_key<DK, 16>(op, mixer, rnd, p, s);
+    case 32: return launch_key<DK, 32>(op, mixer, rnd, p, s);
+    case 64: return launch_key<DK, 64>(op, mixer, rnd, p, s);
+    case 128: return launch_key<DK, 128>(op, mixer, rnd, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace qs

@@ -1,0 +1,12 @@
+// qstate_key_dk64.hip — key-axis kernels for dk = 64.
+
+#include "qstate_key.h"
+
+namespace qs {
+
+hipError_t launch_key_dk64(Op op, int mixer, int rounding, const KParams& p,
+                       hipStream_t stream) {
+  return launch_key_dk<64>(op, mixer, rounding, p, stream);
+}
+
+}  // namespace qs

@@ -1,6 +1,6 @@
 // qstate_launch.h — internal interface between the C ABI (qstate_api.cpp)
-// and the gfx950 kernels (qstate_kernels.hip).  Not installed, not part of
-// the public ABI.
+// and the gfx950 kernels (qstate_value_dk*.hip, qstate_key_dk*.hip).  Not
+// installed, not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -37,8 +37,20 @@ enum Op { kStep = 0, kImport = 1, kExport = 2, kReadout = 3 };
 
 // Launch one kernel over all B*H heads on `stream`.  Returns hipSuccess or
 // the launch error.  mixer/rounding as in qstate.h; fp32 selects the
-// unquantized-state kernels.
+// unquantized-state kernels.  (qstate_dispatch.cpp)
 hipError_t launch(Op op, int mixer, int rounding, int fp32, int dk,
                   const KParams& p, hipStream_t stream);
+
+// Per-dk entry points of the kernel sources (qstate_value_dk*.hip,
+// qstate_key_dk*.hip), one translation unit each.
+hipError_t launch_value_dk64(Op op, int mixer, int rounding, int fp32, const KParams& p,
+                             hipStream_t stream);
+hipError_t launch_value_dk128(Op op, int mixer, int rounding, int fp32, const KParams& p,
+                              hipStream_t stream);
+hipError_t launch_value_dk256(Op op, int mixer, int rounding, int fp32, const KParams& p,
+                              hipStream_t stream);
+hipError_t launch_key_dk64(Op op, int mixer, int rounding, const KParams& p, hipStream_t stream);
+hipError_t launch_key_dk128(Op op, int mixer, int rounding, const KParams& p, hipStream_t stream);
+hipError_t launch_key_dk256(Op op, int mixer, int rounding, const KParams& p, hipStream_t stream);
 
 }  // namespace qs

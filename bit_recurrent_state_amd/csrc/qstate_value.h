@@ -1,0 +1,405 @@
+// qstate_value.h — value-axis decode kernels (scale groups of G key columns
+// inside one value row) and the FP32-state kernels, templated on dk.  Each
+// qstate_value_dk*.hip instantiates one dk.
+
+#pragma once
+
+#include "qstate_device.h"
+
+namespace qs {
+namespace {
+
+// ---------------------------------------------------------------------------
+// The decode step on a quantized head of BITS-bit codes.
+// ---------------------------------------------------------------------------
+
+struct RowIn {
+  uint4 raw;
+  float s0, s1, v;
+};
+
+template <int MIXER, int RND, int DK, int BITS, int G>
+__device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl) {
+  constexpr bool SR = RND == kSR;
+  using Gm = Geo<DK, BITS>;
+  constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr float bias = (float)(1 << (BITS - 1));
+  constexpr bool two_groups = G < E;  // INT4 with G = 16
+  constexpr int LPG = two_groups ? 0 : G / E;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = two_groups ? col0 / 16 : col0 / G;  // first group of the lane in its row
+
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const float* vh = p.v + (size_t)sl.head * p.dv;
+  float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
+
+  // per-head vectors first, so that waiting for them never drains the ring
+  const uint32_t key = SR ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  float alpha_s = 0.0f, beta = 0.0f;
+  if constexpr (vector_decay(MIXER)) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+    alpha_s = p.alpha[sl.head];
+  }
+  if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
+
+  // Every lane always loads an in-range row: rows past the slice (the last
+  // iteration's tail and the prefetches beyond the end) re-read the slice's
+  // last row and are never stored.  Branch-free loads keep the ring's loads
+  // in flight across iterations.
+  auto load = [&](int it) {
+    RowIn in;
+    const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
+    in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+    in.s0 = hscales[(size_t)row * ngr + gcol];
+    in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
+    in.v = vh[row];
+    return in;
+  };
+  RowIn ring[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    ring[k] = load(k);
+    asm volatile("" ::: "memory");  // issue the slots in order: slot 0 is needed first
+  }
+
+  // Trips of kPrefetch iterations.  A slot's next load is issued once its
+  // previous contents (codes, scales, v) are dead, so the load lands in the
+  // same registers and stays in flight across trips.
+  // Iterations past the end compute on clamped rows and store nothing.
+  const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
+  for (int t = 0; t < n_trips; ++t) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int it = t * kPrefetch + k;
+      const int row = sl.r0 + it * RPW + rsub;
+      const bool store_ok = it < n_it && row < sl.r1;
+      const uint32_t w[4] = {ring[k].raw.x, ring[k].raw.y, ring[k].raw.z, ring[k].raw.w};
+      const float s_0 = ring[k].s0, s_1 = ring[k].s1, vrow = ring[k].v;
+      float d[E];
+      unpack16<BITS>(w, d);
+      if constexpr (E == 32) unpack16<BITS>(w + 2, d + 16);
+      // decayed dequantized values (exactly the rounded c*(s*alpha) / (c*s)*alpha_j)
+      if constexpr (vector_decay(MIXER)) {
+        const float nb0 = -bias * s_0, nb1 = -bias * s_1;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+          d[j] = __builtin_fmaf(d[j], j < 16 ? s_0 : s_1, j < 16 ? nb0 : nb1) * al[j];
+      } else {
+        const float sa0 = s_0 * alpha_s, sa1 = s_1 * alpha_s;
+        const float nb0 = -bias * sa0, nb1 = -bias * sa1;
+#pragma unroll
+        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], j < 16 ? sa0 : sa1, j < 16 ? nb0 : nb1);
+      }
+      // write weight
+      float wt;
+      if constexpr (delta_rule(MIXER)) {
+        const float u = row_sum<LPR>(lane_dot(d, kk));
+        wt = beta * (vrow - u);
+      } else if constexpr (MIXER == kGLA) {
+        wt = vrow;
+      } else {
+        wt = beta * vrow;
+      }
+      // rank-1 write (in place) and readout from the full-precision S'
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
+      const float o = row_sum<LPR>(lane_dot(d, qq));
+      // requantize
+      float s0 = s_0, s1 = s_1;
+      const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
+      const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
+      if (store_ok) {
+        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        if constexpr (two_groups) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+          hscales[(size_t)row * ngr + gcol + 1] = s1;
+        } else if (lr % LPG == 0) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+        }
+        if (oh && lr == 0) oh[row] = o;
+      }
+    }
+  }
+}
+
+// The same step on an unquantized FP32 head: 16 elements per lane.
+template <int MIXER, int DK>
+__device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl) {
+  constexpr int E = 16, LPR = DK / E, RPW = 64 / LPR;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  float* hS = reinterpret_cast<float*>(p.state) + (size_t)sl.head * p.dv * DK;
+  const float* vh = p.v + (size_t)sl.head * p.dv;
+  float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
+  struct FIn {
+    float x[E];
+    float v;
+  };
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  float alpha_s = 0.0f, beta = 0.0f;
+  if constexpr (vector_decay(MIXER)) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+    alpha_s = p.alpha[sl.head];
+  }
+  if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
+  // branch-free loads of in-range rows (see step_quant_head)
+  auto load = [&](int it) {
+    FIn in;
+    const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
+    loadv(hS + (size_t)row * DK + col0, in.x);
+    in.v = vh[row];
+    return in;
+  };
+  FIn ring[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    ring[k] = load(k);
+    asm volatile("" ::: "memory");  // issue the slots in order: slot 0 is needed first
+  }
+  const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
+  for (int t = 0; t < n_trips; ++t) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int it = t * kPrefetch + k;
+      const int row = sl.r0 + it * RPW + rsub;
+      const bool store_ok = it < n_it && row < sl.r1;
+      const float vrow = ring[k].v;
+      float d[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = ring[k].x[j] * (vector_decay(MIXER) ? al[j] : alpha_s);
+      float wt;
+      if constexpr (delta_rule(MIXER)) {
+        const float u = row_sum<LPR>(lane_dot(d, kk));
+        wt = beta * (vrow - u);
+      } else if constexpr (MIXER == kGLA) {
+        wt = vrow;
+      } else {
+        wt = beta * vrow;
+      }
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
+      const float o = row_sum<LPR>(lane_dot(d, qq));
+      if (store_ok) {
+        storev(hS + (size_t)row * DK + col0, d);
+        if (oh && lr == 0) oh[row] = o;
+      }
+    }
+  }
+}
+
+// Import (quantize an FP32 state), export (dequantize) and readout of a
+// quantized head, with the step's lane geometry and quantizer.
+template <int OP, bool SR, int DK, int BITS, int G>
+__device__ __forceinline__ void aux_quant_head(const KParams& p, const Slice sl) {
+  using Gm = Geo<DK, BITS>;
+  constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr float bias = (float)(1 << (BITS - 1));
+  constexpr bool two_groups = G < E;
+  constexpr int LPG = two_groups ? 0 : G / E;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = two_groups ? col0 / 16 : col0 / G;
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const size_t hoff = (size_t)sl.head * p.dv * DK;
+  const uint32_t key = (OP == kImport && SR) ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float qq[E];
+  if constexpr (OP == kReadout) loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  for (int rbase = sl.r0; rbase < sl.r1; rbase += RPW) {
+    const int row = rbase + rsub;
+    const bool ok = row < sl.r1;
+    if constexpr (OP == kImport) {
+      float x[E];
+      if (ok)
+        loadv(p.src + hoff + (size_t)row * DK + col0, x);
+      else
+#pragma unroll
+        for (int j = 0; j < E; ++j) x[j] = 0.0f;
+      float s0 = 0.0f, s1 = 0.0f;
+      const uint32_t no_prev[4] = {0u, 0u, 0u, 0u};  // read only by BDR, never on import
+      const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
+      const uint4 packed =
+          quantize_lane<BITS, SR ? kSR : kRTN, E, LPG>(x, key, block0, no_prev, s0, s1);
+      if (ok) {
+        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        if constexpr (two_groups) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+          hscales[(size_t)row * ngr + gcol + 1] = s1;
+        } else if (lr % LPG == 0) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+        }
+      }
+    } else {
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      float s0 = 0.0f, s1 = 0.0f;
+      if (ok) {
+        raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+        s0 = hscales[(size_t)row * ngr + gcol];
+        s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : s0;
+      }
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float x[E];
+      unpack16<BITS>(w, x);
+      if constexpr (E == 32) unpack16<BITS>(w + 2, x + 16);
+      const float nb0 = -bias * s0, nb1 = -bias * s1;
+#pragma unroll
+      for (int j = 0; j < E; ++j) x[j] = __builtin_fmaf(x[j], j < 16 ? s0 : s1, j < 16 ? nb0 : nb1);
+      if constexpr (OP == kExport) {
+        if (ok) storev(p.dst + hoff + (size_t)row * DK + col0, x);
+      } else {
+        const float o = row_sum<LPR>(lane_dot(x, qq));
+        if (ok && lr == 0) p.o[(size_t)sl.head * p.dv + row] = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels and dispatch.
+// ---------------------------------------------------------------------------
+
+template <int MIXER, int RND, int DK, int G>
+__global__ __launch_bounds__(kThreads) void step_kernel(const KParams p) {
+  const Slice sl = wave_slice(p);
+  if (head_is_int8(p, sl.h))
+    step_quant_head<MIXER, RND, DK, 8, G>(p, sl);
+  else
+    step_quant_head<MIXER, RND, DK, 4, G>(p, sl);
+}
+
+template <int MIXER, int DK>
+__global__ __launch_bounds__(kThreads) void step_fp32_kernel(const KParams p) {
+  step_fp32_head<MIXER, DK>(p, wave_slice(p));
+}
+
+template <int OP, bool SR, int DK, int G>
+__global__ __launch_bounds__(kThreads) void aux_kernel(const KParams p) {
+  const Slice sl = wave_slice(p);
+  if (head_is_int8(p, sl.h))
+    aux_quant_head<OP, SR, DK, 8, G>(p, sl);
+  else
+    aux_quant_head<OP, SR, DK, 4, G>(p, sl);
+}
+
+template <int DK>
+__global__ __launch_bounds__(kThreads) void readout_fp32_kernel(const KParams p) {
+  constexpr int E = 16, LPR = DK / E, RPW = 64 / LPR;
+  const Slice sl = wave_slice(p);
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  float qq[E];
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  const float* hS = reinterpret_cast<const float*>(p.state) + (size_t)sl.head * p.dv * DK;
+  for (int rbase = sl.r0; rbase < sl.r1; rbase += RPW) {
+    const int row = rbase + rsub;
+    float x[E];
+    if (row < sl.r1)
+      loadv(hS + (size_t)row * DK + col0, x);
+    else
+#pragma unroll
+      for (int j = 0; j < E; ++j) x[j] = 0.0f;
+    const float o = row_sum<LPR>(lane_dot(x, qq));
+    if (row < sl.r1 && lr == 0) p.o[(size_t)sl.head * p.dv + row] = o;
+  }
+}
+
+inline dim3 grid_of(const KParams& p) { return dim3((unsigned)(p.B * p.H * p.slices)); }
+
+template <int DK, int G>
+hipError_t launch_quant(Op op, int mixer, int rnd, const KParams& p, hipStream_t s) {
+  const dim3 grid = grid_of(p), block(kThreads);
+  if (op == kStep) {
+#define QS_STEP(M)                                                    \
+  if (mixer == M) {                                                   \
+    switch (rnd) {                                                    \
+      case kRTN: step_kernel<M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
+      case kSR: step_kernel<M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
+      case kBDR: step_kernel<M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
+      default: return hipErrorInvalidValue;                           \
+    }                                                                 \
+    return hipGetLastError();                                         \
+  }
+    QS_STEP(kGDN) QS_STEP(kGLA) QS_STEP(kScalar) QS_STEP(kKDA)
+#undef QS_STEP
+    return hipErrorInvalidValue;
+  }
+  switch (op) {
+    case kImport:  // nothing stored before an import: BDR rounds to nearest
+      if (rnd == kSR)
+        aux_kernel<kImport, true, DK, G><<<grid, block, 0, s>>>(p);
+      else
+        aux_kernel<kImport, false, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    case kExport:
+      aux_kernel<kExport, false, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    case kReadout:
+      aux_kernel<kReadout, false, DK, G><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// Key-axis groups: workgroups of KGeo::NW waves over blocks of KGeo::BR rows.
+template <int DK>
+hipError_t launch_value_dk(Op op, int mixer, int rnd, int fp32, const KParams& p, hipStream_t s) {
+  const dim3 grid = grid_of(p), block(kThreads);
+  if (fp32) {
+    if (op == kStep) {
+      switch (mixer) {
+        case kGDN: step_fp32_kernel<kGDN, DK><<<grid, block, 0, s>>>(p); break;
+        case kGLA: step_fp32_kernel<kGLA, DK><<<grid, block, 0, s>>>(p); break;
+        case kScalar: step_fp32_kernel<kScalar, DK><<<grid, block, 0, s>>>(p); break;
+        case kKDA: step_fp32_kernel<kKDA, DK><<<grid, block, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+    if (op == kReadout) {
+      readout_fp32_kernel<DK><<<grid, block, 0, s>>>(p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;  // import/export of an FP32 state are plain copies
+  }
+  if (p.slice_rows % 32 != 0) return hipErrorInvalidValue;
+  switch (p.G) {
+    case 16: return launch_quant<DK, 16>(op, mixer, rnd, p, s);
+    case 32: return launch_quant<DK, 32>(op, mixer, rnd, p, s);
+    case 64: return launch_quant<DK, 64>(op, mixer, rnd, p, s);
+    case 128: return launch_quant<DK, 128>(op, mixer, rnd, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace qs

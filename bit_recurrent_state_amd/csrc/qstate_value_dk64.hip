@@ -1,0 +1,12 @@
+// qstate_value_dk64.hip — value-axis and FP32-state kernels for dk = 64.
+
+#include "qstate_value.h"
+
+namespace qs {
+
+hipError_t launch_value_dk64(Op op, int mixer, int rounding, int fp32, const KParams& p,
+                         hipStream_t stream) {
+  return launch_value_dk<64>(op, mixer, rounding, fp32, p, stream);
+}
+
+}  // namespace qs
