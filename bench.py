@@ -39,11 +39,16 @@ KERNEL_SRCS = [os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", f)
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the decode kernels' source (all scale-group layouts)."""
+    """sha256[:16] of the decode kernels' code (all scale-group layouts), with
+    // comments and blank lines dropped so that comment edits keep it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+        for line in open(f).read().splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -4,20 +4,6 @@
 // 16-element chunks, per-head geometry.  Included by each kernel source;
 // everything here has internal linkage.
 //
-// One wave (a workgroup of 64 lanes) owns a slice of the rows of one head
-// (b, h); small batches split a head into several slices so that enough
-// waves exist to fill 256 CUs.  A value row of the state is split across
-// adjacent lanes: each lane owns one 16-byte run of codes, i.e. 16 INT8
-// elements or 32 INT4 elements, so a row of dk columns spans dk/16 (INT8) or
-// dk/32 (INT4) lanes and the wave holds the rest of its 64 lanes as further
-// rows.  The loads of the next kPrefetch row iterations are in flight while
-// the current one is computed.  Every operation of the step is row-local (LoReS
-// blog, "LoReS: State Quantization": value-axis groups, full-precision update,
-// readout from the updated state): the two dot products u = d.k and o = S'.q
-// finish with DPP butterflies across the row's lanes, the group absmax with
-// DPP butterflies across the group's lanes.  No LDS, no atomics, no
-// cross-workgroup traffic: each state byte is read once and written once.
-//
 // Arithmetic follows the semantics written in include/qstate.h operation by
 // operation (explicit fmaf, no contraction, IEEE division), so the stored
 // codes are bit-identical to any other implementation of those semantics.
