@@ -69,12 +69,12 @@ def lib():
             "oracle_head_offset": (ctypes.c_size_t, [cp, _P, i32, i32]),
             "oracle_get_code": (i32, [_P, i32, ctypes.c_int64]),
             "oracle_set_code": (None, [_P, i32, ctypes.c_int64, i32]),
-            "oracle_head_step": (None, [cp, i32, i32, i32, _P, _P, _P, _P, _P, _P, f32,
+            "oracle_head_step": (None, [cp, i32, i32, _P, _P, _P, _P, _P, _P, _P, f32,
                                         _P, u64, _P, _P]),
             "oracle_head_step_fp32": (None, [cp, _P, _P, _P, _P, _P, f32, _P]),
-            "oracle_head_quantize": (None, [cp, i32, i32, i32, _P, _P, _P, u64, _P]),
-            "oracle_head_dequantize": (None, [cp, i32, _P, _P, _P]),
-            "oracle_head_readout": (None, [cp, i32, _P, _P, _P, _P]),
+            "oracle_head_quantize": (None, [cp, i32, i32, _P, _P, _P, _P, u64, _P]),
+            "oracle_head_dequantize": (None, [cp, _P, _P, _P, _P]),
+            "oracle_head_readout": (None, [cp, _P, _P, _P, _P, _P]),
             "oracle_step": (None, [cp, _P, _P, _P, _P, _P, _P, _P, _P, _P, u64]),
             "oracle_step_fp32": (None, [cp, _P, _P, _P, _P, _P, _P, _P]),
             "oracle_quantize": (None, [cp, _P, _P, _P, _P, u64]),
@@ -110,11 +110,32 @@ def scales_shape(c: Cfg):
 
 
 def head_bits_array(c: Cfg, head_bits=None) -> np.ndarray:
+    """Bit widths per head and 16-column block, [H][dk/16]: from None (all
+    INT8), one width per head [H], or per block [H][dk/16]."""
+    nb = c.dk // 16
     if head_bits is None:
-        return np.full(c.H, 8, dtype=np.uint8)
-    hb = np.ascontiguousarray(head_bits, dtype=np.uint8)
-    assert hb.shape == (c.H,)
-    return hb
+        return np.full((c.H, nb), 8, dtype=np.uint8)
+    hb = np.asarray(head_bits, dtype=np.uint8)
+    if hb.ndim == 1:
+        assert hb.shape == (c.H,)
+        hb = np.repeat(hb[:, None], nb, axis=1)
+    assert hb.shape == (c.H, nb)
+    return np.ascontiguousarray(hb)
+
+
+def block_bits(c: Cfg, bits) -> np.ndarray:
+    """Widths of one head's 16-column blocks, from one width or a block list."""
+    nb = c.dk // 16
+    bb = np.asarray(bits, dtype=np.uint8).reshape(-1)
+    if bb.size == 1:
+        bb = np.full(nb, bb[0], np.uint8)
+    assert bb.shape == (nb,)
+    return np.ascontiguousarray(bb)
+
+
+def head_code_bytes(c: Cfg, bits) -> int:
+    """Code bytes of one head with the given width(s)."""
+    return int(c.dv * np.sum(block_bits(c, bits).astype(np.int64) * 2))
 
 
 # ---- scalar pieces -------------------------------------------------------
@@ -198,7 +219,8 @@ def head_step(c: Cfg, b, h, bits, codes, scales, q, k, v, alpha, beta, step,
     Returns (o, pre, xval) with pre/xval None unless requested."""
     assert codes.dtype == np.uint8 and codes.flags.c_contiguous
     assert scales.dtype == np.float32 and scales.flags.c_contiguous
-    assert codes.size == c.dv * c.dk * bits // 8
+    bb = block_bits(c, bits)
+    assert codes.size == head_code_bytes(c, bb)
     assert scales.size == int(np.prod(scales_shape(c)))
     q, k, v, alpha = _f32(q), _f32(k), _f32(v), _f32(alpha)
     assert q.size == c.dk and k.size == c.dk and v.size == c.dv
@@ -206,7 +228,7 @@ def head_step(c: Cfg, b, h, bits, codes, scales, q, k, v, alpha, beta, step,
     o = np.zeros(c.dv, np.float32)
     pre = np.zeros((c.dv, c.dk), np.float32) if want_pre else None
     xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
-    lib().oracle_head_step(ctypes.byref(c), b, h, bits, _ptr(codes), _ptr(scales), _ptr(q),
+    lib().oracle_head_step(ctypes.byref(c), b, h, _ptr(bb), _ptr(codes), _ptr(scales), _ptr(q),
                            _ptr(k), _ptr(v), _ptr(alpha), float(beta), _ptr(o), step,
                            _ptr(pre), _ptr(xval))
     return o, pre, xval
@@ -224,24 +246,27 @@ def head_step_fp32(c: Cfg, S, q, k, v, alpha, beta):
 def head_quantize(c: Cfg, b, h, bits, S, step, want_xval=False):
     S = _f32(S)
     assert S.size == c.dv * c.dk
-    codes = np.zeros(c.dv * c.dk * bits // 8, np.uint8)
+    bb = block_bits(c, bits)
+    codes = np.zeros(head_code_bytes(c, bb), np.uint8)
     scales = np.zeros(int(np.prod(scales_shape(c))), np.float32)
     xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
-    lib().oracle_head_quantize(ctypes.byref(c), b, h, bits, _ptr(S), _ptr(codes),
+    lib().oracle_head_quantize(ctypes.byref(c), b, h, _ptr(bb), _ptr(S), _ptr(codes),
                                _ptr(scales), step, _ptr(xval))
     return codes, scales, xval
 
 
 def head_dequantize(c: Cfg, bits, codes, scales):
     S = np.zeros((c.dv, c.dk), np.float32)
-    lib().oracle_head_dequantize(ctypes.byref(c), bits, _ptr(np.ascontiguousarray(codes)),
+    lib().oracle_head_dequantize(ctypes.byref(c), _ptr(block_bits(c, bits)),
+                                 _ptr(np.ascontiguousarray(codes)),
                                  _ptr(_f32(scales)), _ptr(S))
     return S
 
 
 def head_readout(c: Cfg, bits, codes, scales, q):
     o = np.zeros(c.dv, np.float32)
-    lib().oracle_head_readout(ctypes.byref(c), bits, _ptr(np.ascontiguousarray(codes)),
+    lib().oracle_head_readout(ctypes.byref(c), _ptr(block_bits(c, bits)),
+                              _ptr(np.ascontiguousarray(codes)),
                               _ptr(_f32(scales)), _ptr(_f32(q)), _ptr(o))
     return o
 

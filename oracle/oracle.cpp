@@ -162,27 +162,75 @@ int oracle_round_bdr(float x, float inv, float s_new, float prev, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// Layout: codes of head (b, h) start at b*P + sum_{h'<h} dv*dk*bits_h'/8.
-// INT8 codes are int8; INT4 codes are two's-complement nibbles, even element
-// in the low nibble.
+// Layout.  Bit widths are given per block of 16 key columns of a head
+// (LoReS 2/4: more bits for the slowest-decaying heads or channels; a head
+// with one width has all its blocks alike).  A value row stores its blocks in
+// column order, 16 bytes for an INT8 block and 8 for an INT4 block; rows are
+// contiguous, heads follow each other in (b, h) order.  INT8 codes are int8;
+// INT4 codes are two's-complement nibbles, even column in the low nibble.
 // ---------------------------------------------------------------------------
 
-static size_t head_bytes(const oracle_cfg* c, int bits) {
-  return (size_t)c->dv * (size_t)c->dk * (size_t)bits / 8;
+namespace {
+
+struct Layout {
+  int nb = 0;            // blocks of 16 key columns
+  int bits[16] = {};     // width of each block
+  size_t off[16] = {};   // byte offset of each block inside a row
+  size_t row_bytes = 0;
+};
+
+Layout head_layout(const oracle_cfg* c, const uint8_t* block_bits) {
+  Layout L;
+  L.nb = c->dk / 16;
+  for (int q = 0; q < L.nb; ++q) {
+    L.bits[q] = block_bits[q];
+    L.off[q] = L.row_bytes;
+    L.row_bytes += (size_t)16 * block_bits[q] / 8;
+  }
+  return L;
 }
 
-size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* head_bits) {
+int get_code_at(const Layout& L, const uint8_t* codes, int i, int j) {
+  const int q = j / 16, t = j % 16;
+  const uint8_t* row = codes + (size_t)i * L.row_bytes + L.off[q];
+  if (L.bits[q] == 8) return (int)(int8_t)row[t];
+  const uint8_t byte = row[t / 2];
+  const int nib = (t % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+void set_code_at(const Layout& L, uint8_t* codes, int i, int j, int code) {
+  const int q = j / 16, t = j % 16;
+  uint8_t* row = codes + (size_t)i * L.row_bytes + L.off[q];
+  if (L.bits[q] == 8) {
+    row[t] = (uint8_t)(int8_t)code;
+    return;
+  }
+  const uint8_t nib = (uint8_t)(code & 0xF);
+  uint8_t& byte = row[t / 2];
+  byte = (t % 2 == 0) ? (uint8_t)((byte & 0xF0) | nib) : (uint8_t)((byte & 0x0F) | (nib << 4));
+}
+
+}  // namespace
+
+static size_t head_bytes(const oracle_cfg* c, const uint8_t* block_bits) {
+  return (size_t)c->dv * head_layout(c, block_bits).row_bytes;
+}
+
+size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* block_bits) {
+  const int nb = c->dk / 16;
   size_t per_b = 0;
-  for (int h = 0; h < c->H; ++h) per_b += head_bytes(c, head_bits[h]);
+  for (int h = 0; h < c->H; ++h) per_b += head_bytes(c, block_bits + (size_t)h * nb);
   return per_b * (size_t)c->B;
 }
 
-size_t oracle_head_offset(const oracle_cfg* c, const uint8_t* head_bits, int b,
-                          int h) {
+size_t oracle_head_offset(const oracle_cfg* c, const uint8_t* block_bits, int b, int h) {
+  const int nb = c->dk / 16;
   size_t per_b = 0, before = 0;
   for (int hh = 0; hh < c->H; ++hh) {
-    if (hh < h) before += head_bytes(c, head_bits[hh]);
-    per_b += head_bytes(c, head_bits[hh]);
+    const size_t n = head_bytes(c, block_bits + (size_t)hh * nb);
+    if (hh < h) before += n;
+    per_b += n;
   }
   return (size_t)b * per_b + before;
 }
@@ -232,11 +280,13 @@ static size_t scale_index(const oracle_cfg* c, int i, int j) {
 // S, with scale slot si.  prev: the head's stored values before the step
 // (BDR); NULL for an import, where BDR has nothing to compare with and
 // rounds to nearest.
-static void quantize_group(const oracle_cfg* c, int bits, uint32_t key,
+// All elements of a group share one width (a value-axis group lies inside
+// blocks of one width; a key-axis group is one column).
+static void quantize_group(const oracle_cfg* c, const Layout& L, uint32_t key,
                            const std::vector<int64_t>& e, size_t si,
                            const float* S, const float* prev, uint8_t* codes,
                            float* scales, double* xval) {
-  const int r = qmax(bits);
+  const int r = qmax(L.bits[(int)(e[0] % c->dk) / 16]);
   float m = 0.0f;
   for (int64_t x : e) m = std::max(m, std::fabs(S[x]));
   float s, inv;
@@ -259,11 +309,11 @@ static void quantize_group(const oracle_cfg* c, int bits, uint32_t key,
       if (xval) xval[x] = (double)S[x] * (double)inv;
     }
     n = std::max(-r, std::min(r, n));
-    oracle_set_code(codes, bits, x, n);
+    set_code_at(L, codes, (int)(x / c->dk), (int)(x % c->dk), n);
   }
 }
 
-static void quantize_head(const oracle_cfg* c, int bits, uint32_t key,
+static void quantize_head(const oracle_cfg* c, const Layout& L, uint32_t key,
                           const float* S, const float* prev, uint8_t* codes,
                           float* scales, double* xval) {
   const int dk = c->dk, dv = c->dv, G = c->G;
@@ -272,13 +322,13 @@ static void quantize_head(const oracle_cfg* c, int bits, uint32_t key,
     for (int g = 0; g < dv / G; ++g)
       for (int j = 0; j < dk; ++j) {
         for (int t = 0; t < G; ++t) e[t] = (int64_t)(g * G + t) * dk + j;
-        quantize_group(c, bits, key, e, scale_index(c, g * G, j), S, prev, codes, scales, xval);
+        quantize_group(c, L, key, e, scale_index(c, g * G, j), S, prev, codes, scales, xval);
       }
   } else {
     for (int i = 0; i < dv; ++i)
       for (int g = 0; g < dk / G; ++g) {
         for (int t = 0; t < G; ++t) e[t] = (int64_t)i * dk + g * G + t;
-        quantize_group(c, bits, key, e, scale_index(c, i, g * G), S, prev, codes, scales, xval);
+        quantize_group(c, L, key, e, scale_index(c, i, g * G), S, prev, codes, scales, xval);
       }
   }
 }
@@ -295,12 +345,13 @@ static void quantize_head(const oracle_cfg* c, int bits, uint32_t key,
 // (I - b k k^T) + b v k^T.  Readout o = S' q from the unquantized S'.
 // ---------------------------------------------------------------------------
 
-void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
+void oracle_head_step(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                       uint8_t* codes, float* scales, const float* q,
                       const float* k, const float* v, const float* alpha,
                       float beta, float* o, uint64_t step, float* pre,
                       double* xval) {
   const int dk = c->dk, dv = c->dv;
+  const Layout L = head_layout(c, block_bits);
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
   std::vector<float> d(dk), Sp((size_t)dv * dk), stored((size_t)dv * dk);
   for (int i = 0; i < dv; ++i) {
@@ -308,7 +359,7 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
     // dequantize and decay
     for (int j = 0; j < dk; ++j) {
       const int64_t x = (int64_t)i * dk + j;
-      const float code = (float)oracle_get_code(codes, bits, x);
+      const float code = (float)get_code_at(L, codes, i, j);
       const float s = scales[scale_index(c, i, j)];
       stored[x] = code * s;
       if (vector_decay(c->mixer))
@@ -331,7 +382,7 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
     if (o) o[i] = oracle_dot(sp, q, dk);
   }
   if (pre) std::memcpy(pre, Sp.data(), sizeof(float) * Sp.size());
-  quantize_head(c, bits, key, Sp.data(), stored.data(), codes, scales, xval);
+  quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, xval);
 }
 
 // The same step on an unquantized FP32 state (the "FP32 states" the pages
@@ -359,26 +410,26 @@ void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
   }
 }
 
-void oracle_head_quantize(const oracle_cfg* c, int b, int h, int bits,
+void oracle_head_quantize(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                           const float* S, uint8_t* codes, float* scales,
                           uint64_t step, double* xval) {
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
-  quantize_head(c, bits, key, S, nullptr, codes, scales, xval);
+  quantize_head(c, head_layout(c, block_bits), key, S, nullptr, codes, scales, xval);
 }
 
-void oracle_head_dequantize(const oracle_cfg* c, int bits, const uint8_t* codes,
-                            const float* scales, float* S) {
+void oracle_head_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
+                            const uint8_t* codes, const float* scales, float* S) {
   const int dk = c->dk;
+  const Layout L = head_layout(c, block_bits);
   for (int i = 0; i < c->dv; ++i)
     for (int j = 0; j < dk; ++j)
-      S[(size_t)i * dk + j] = (float)oracle_get_code(codes, bits, (int64_t)i * dk + j) *
-                              scales[scale_index(c, i, j)];
+      S[(size_t)i * dk + j] = (float)get_code_at(L, codes, i, j) * scales[scale_index(c, i, j)];
 }
 
-void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
+void oracle_head_readout(const oracle_cfg* c, const uint8_t* block_bits, const uint8_t* codes,
                          const float* scales, const float* q, float* o) {
   std::vector<float> S((size_t)c->dv * c->dk);
-  oracle_head_dequantize(c, bits, codes, scales, S.data());
+  oracle_head_dequantize(c, block_bits, codes, scales, S.data());
   for (int i = 0; i < c->dv; ++i) o[i] = oracle_dot(S.data() + (size_t)i * c->dk, q, c->dk);
 }
 
@@ -386,7 +437,7 @@ void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
 // Whole batch, in the library's array layout.
 // ---------------------------------------------------------------------------
 
-void oracle_step(const oracle_cfg* c, const uint8_t* head_bits, uint8_t* codes,
+void oracle_step(const oracle_cfg* c, const uint8_t* block_bits, uint8_t* codes,
                  float* scales, const float* q, const float* k, const float* v,
                  const float* alpha, const float* beta, float* o, uint64_t step) {
   const int dk = c->dk, dv = c->dv;
@@ -394,7 +445,8 @@ void oracle_step(const oracle_cfg* c, const uint8_t* head_bits, uint8_t* codes,
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
-      oracle_head_step(c, b, h, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
+      const uint8_t* bb = block_bits + (size_t)h * (dk / 16);
+      oracle_head_step(c, b, h, bb, codes + oracle_head_offset(c, block_bits, b, h),
                        scales + bh * head_scales(c), q + bh * dk, k + bh * dk, v + bh * dv,
                        alpha + bh * na, (c->mixer == kMixerGLA) ? 0.0f : beta[bh],
                        o ? o + bh * dv : nullptr, step, nullptr, nullptr);
@@ -414,36 +466,38 @@ void oracle_step_fp32(const oracle_cfg* c, float* S, const float* q, const float
     }
 }
 
-void oracle_quantize(const oracle_cfg* c, const uint8_t* head_bits, const float* S,
+void oracle_quantize(const oracle_cfg* c, const uint8_t* block_bits, const float* S,
                      uint8_t* codes, float* scales, uint64_t step) {
   const int dk = c->dk, dv = c->dv;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
-      oracle_head_quantize(c, b, h, head_bits[h], S + bh * dv * dk,
-                           codes + oracle_head_offset(c, head_bits, b, h),
+      oracle_head_quantize(c, b, h, block_bits + (size_t)h * (dk / 16), S + bh * dv * dk,
+                           codes + oracle_head_offset(c, block_bits, b, h),
                            scales + bh * head_scales(c), step, nullptr);
     }
 }
 
-void oracle_dequantize(const oracle_cfg* c, const uint8_t* head_bits,
+void oracle_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
                        const uint8_t* codes, const float* scales, float* S) {
   const int dk = c->dk, dv = c->dv;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
-      oracle_head_dequantize(c, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
+      oracle_head_dequantize(c, block_bits + (size_t)h * (dk / 16),
+                             codes + oracle_head_offset(c, block_bits, b, h),
                              scales + bh * head_scales(c), S + bh * dv * dk);
     }
 }
 
-void oracle_readout(const oracle_cfg* c, const uint8_t* head_bits, const uint8_t* codes,
+void oracle_readout(const oracle_cfg* c, const uint8_t* block_bits, const uint8_t* codes,
                     const float* scales, const float* q, float* o) {
   const int dk = c->dk, dv = c->dv;
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t bh = (size_t)b * c->H + h;
-      oracle_head_readout(c, head_bits[h], codes + oracle_head_offset(c, head_bits, b, h),
+      oracle_head_readout(c, block_bits + (size_t)h * (dk / 16),
+                          codes + oracle_head_offset(c, block_bits, b, h),
                           scales + bh * head_scales(c), q + bh * dk, o + bh * dv);
     }
 }

@@ -57,9 +57,12 @@ int oracle_round_rtn(float x, float inv);
 int oracle_round_sr(float x, float inv, uint32_t r16);
 int oracle_round_bdr(float x, float inv, float s_new, float prev, int r);
 
-/* ---- layout ---- */
-size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* head_bits);
-size_t oracle_head_offset(const oracle_cfg* c, const uint8_t* head_bits,
+/* ---- layout ----
+ * Bit widths come per block of 16 key columns: block_bits of one head holds
+ * dk/16 entries (4 or 8); the batch functions take [H][dk/16].  A row stores
+ * its blocks in column order (16 bytes per INT8 block, 8 per INT4 block). */
+size_t oracle_codes_bytes(const oracle_cfg* c, const uint8_t* block_bits);
+size_t oracle_head_offset(const oracle_cfg* c, const uint8_t* block_bits,
                           int b, int h);
 int oracle_get_code(const uint8_t* head_codes, int bits, int64_t e);
 void oracle_set_code(uint8_t* head_codes, int bits, int64_t e, int code);
@@ -70,7 +73,7 @@ void oracle_set_code(uint8_t* head_codes, int bits, int64_t e, int code);
  * o, pre, xval may be NULL.  pre receives S' [dv][dk] before requantizing;
  * xval receives the pre-rounding value per element (RTN: the exact product
  * S'*inv; SR: fma(S', inv, u)). */
-void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
+void oracle_head_step(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                       uint8_t* codes, float* scales, const float* q,
                       const float* k, const float* v, const float* alpha,
                       float beta, float* o, uint64_t step, float* pre,
@@ -78,29 +81,29 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, int bits,
 void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
                            const float* k, const float* v, const float* alpha,
                            float beta, float* o);
-void oracle_head_quantize(const oracle_cfg* c, int b, int h, int bits,
+void oracle_head_quantize(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                           const float* S, uint8_t* codes, float* scales,
                           uint64_t step, double* xval);
-void oracle_head_dequantize(const oracle_cfg* c, int bits,
+void oracle_head_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
                             const uint8_t* codes, const float* scales,
                             float* S);
-void oracle_head_readout(const oracle_cfg* c, int bits, const uint8_t* codes,
+void oracle_head_readout(const oracle_cfg* c, const uint8_t* block_bits, const uint8_t* codes,
                          const float* scales, const float* q, float* o);
 
 /* ---- every head of a [B][H] batch, arrays in the library's layout ---- */
-void oracle_step(const oracle_cfg* c, const uint8_t* head_bits,
+void oracle_step(const oracle_cfg* c, const uint8_t* block_bits,
                  uint8_t* codes, float* scales, const float* q,
                  const float* k, const float* v, const float* alpha,
                  const float* beta, float* o, uint64_t step);
 void oracle_step_fp32(const oracle_cfg* c, float* S, const float* q,
                       const float* k, const float* v, const float* alpha,
                       const float* beta, float* o);
-void oracle_quantize(const oracle_cfg* c, const uint8_t* head_bits,
+void oracle_quantize(const oracle_cfg* c, const uint8_t* block_bits,
                      const float* S, uint8_t* codes, float* scales,
                      uint64_t step);
-void oracle_dequantize(const oracle_cfg* c, const uint8_t* head_bits,
+void oracle_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
                        const uint8_t* codes, const float* scales, float* S);
-void oracle_readout(const oracle_cfg* c, const uint8_t* head_bits,
+void oracle_readout(const oracle_cfg* c, const uint8_t* block_bits,
                     const uint8_t* codes, const float* scales, const float* q,
                     float* o);
 
