@@ -80,12 +80,28 @@ def gate_bytes(w) -> int:
     return alpha + (0 if w.mixer == W.GLA else 4)
 
 
-def algorithmic_bytes(w, hb) -> int:
+def block_bits(w, Q) -> np.ndarray:
+    """Widths per head and 16-column block [H][dk/16] from the workload's
+    decay-based policy (per head, or per group of G key channels)."""
+    import workloads as W
+    nb = w.dk // 16
+    if w.bits_policy == "channel_half":
+        ret = W.group_retention(w)
+        return np.stack([np.repeat(Q.qstate_bits_by_decay(ret[h], 1, 0.5), w.G // 16)
+                         for h in range(w.H)]).astype(np.uint8)
+    policy = {"alpha_gt_0.99": (0, 0.99), "rank_half": (1, 0.5)}.get(w.bits_policy)
+    hb = (Q.qstate_bits_by_decay(W.head_retention(w), *policy) if policy
+          else np.full(w.H, 8, np.uint8))
+    return np.repeat(hb[:, None], nb, axis=1).astype(np.uint8)
+
+
+def algorithmic_bytes(w, bb) -> int:
     """Bytes one step must move: each head's codes and scales read and written
-    once, q, k, v, o, and the gates (alpha per head or per key channel, beta)."""
+    once, q, k, v, o, and the gates (alpha per head or per key channel, beta).
+    bb: widths per head and 16-column block."""
     per_b = 0
     for h in range(w.H):
-        state = w.dv * w.dk * int(hb[h]) // 8 + w.dv * w.dk // w.G * 4
+        state = w.dv * int(np.sum(2 * bb[h].astype(np.int64))) + w.dv * w.dk // w.G * 4
         io = 4 * (2 * w.dk + 2 * w.dv)
         per_b += 2 * state + io + gate_bytes(w)
     return per_b * w.B
@@ -112,10 +128,10 @@ def cpu_baseline(w, hb, seconds: float):
     while time.perf_counter() - t0 < seconds:
         b, h = heads[n % len(heads)]
         if (b, h) not in states:
-            states[(b, h)] = oracle.head_quantize(c, b, h, int(hb[h]), S0, 0)[:2]
+            states[(b, h)] = oracle.head_quantize(c, b, h, hb[h], S0, 0)[:2]
         codes, scales = states[(b, h)]
         a = alpha[b, h] if w.mixer in (W.GLA, W.KDA) else np.float32([alpha[b, h]])
-        oracle.head_step(c, b, h, int(hb[h]), codes, scales, q[b, h], k[b, h], v[b, h], a,
+        oracle.head_step(c, b, h, hb[h], codes, scales, q[b, h], k[b, h], v[b, h], a,
                          0.0 if beta is None else float(beta[b, h]), 1 + n)
         n += 1
     dt = time.perf_counter() - t0
@@ -164,13 +180,16 @@ def main():
     if args.rounding is not None:
         w = w.scaled(rounding=args.rounding)
     w = w.scaled(axis=args.axis)
-    policy = {"alpha_gt_0.99": (0, 0.99), "rank_half": (1, 0.5)}.get(w.bits_policy)
-    hb = (Q.qstate_bits_by_decay(W.head_retention(w), *policy) if policy
-          else np.full(w.H, 8, np.uint8))
+    hb = block_bits(w, Q)  # [H][dk/16]
+    uniform = bool(np.all(hb == hb[:, :1]))
     nbytes = algorithmic_bytes(w, hb)
 
-    cfg0 = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0, 0,
-                    w.axis)
+    def qcfg(layer):
+        return Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False,
+                        hb[:, 0].tolist() if uniform else None, 0, layer, w.axis,
+                        None if uniform else hb.tolist())
+
+    cfg0 = qcfg(0)
     cb, sb = Q.qstate_state_bytes(cfg0)
     n_states = args.states or max(2, int(np.ceil(1.0 * 2**30 / (cb + sb))))
 
@@ -189,9 +208,7 @@ def main():
     f.close()
     states = []
     for layer in range(n_states):
-        cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False, hb.tolist(), 0,
-                       layer, w.axis)
-        s = Q.QState(cfg)
+        s = Q.QState(qcfg(layer))
         s.load_fp32(S)
         states.append(s)
     del S
@@ -230,7 +247,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "group": w.G,
-            "state_bits": {str(b): int((hb == b).sum()) for b in sorted(set(hb.tolist()))},
+            "state_bits": ({str(b): int((hb[:, 0] == b).sum()) for b in sorted(set(hb[:, 0].tolist()))}
+                           if uniform else
+                           {f"{b}-bit 16-channel blocks": int((hb == b).sum())
+                            for b in sorted(set(hb.ravel().tolist()))}),
             "rounding": ROUNDING_NAMES[w.rounding],
             "group_axis": "key" if w.axis else "value", "state_instances": n_states,
             "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,

@@ -18,9 +18,9 @@
 #include "qstate_launch.h"
 
 struct qstate {
-  qstate_config cfg;      // head_bits pointer replaced by bits[]
-  uint8_t bits[256];
-  uint32_t int8_mask[8];
+  qstate_config cfg;          // head_bits / channel_bits pointers cleared
+  uint16_t int8_blocks[256];  // per head: bit q set = 16-column block q is INT8
+  uint32_t head_units[256];   // per head: byte offset in a batch row / (8 dv)
   void* state;            // codes or FP32 state (device)
   float* scales;          // device, quantized only
   uint64_t step;
@@ -34,6 +34,20 @@ constexpr int kMaxDv = 4096;
 constexpr int64_t kTargetWaves = 4096;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Width of block q (16 key columns) of head h: channel_bits, else head_bits,
+// else INT8.
+int block_width(const qstate_config* c, int h, int q) {
+  if (c->channel_bits) return c->channel_bits[(size_t)h * (c->dk / 16) + q];
+  return c->head_bits ? c->head_bits[h] : 8;
+}
+
+uint16_t int8_blocks(const qstate_config* c, int h) {
+  uint16_t m = 0;
+  for (int q = 0; q < c->dk / 16; ++q)
+    if (block_width(c, h, q) == 8) m = (uint16_t)(m | (1u << q));
+  return m;
+}
 
 int check_config(const qstate_config* c) {
   if (!c) return QSTATE_E_INVALID;
@@ -50,6 +64,18 @@ int check_config(const qstate_config* c) {
     if (c->head_bits)
       for (int h = 0; h < c->heads && h < kMaxHeads; ++h)
         if (c->head_bits[h] != 4 && c->head_bits[h] != 8) return QSTATE_E_INVALID;
+    if (c->channel_bits && c->dk % 16 == 0 && c->dk <= 256) {
+      const int nb = c->dk / 16;
+      for (int h = 0; h < c->heads && h < kMaxHeads; ++h)
+        for (int q = 0; q < nb; ++q) {
+          const int w = c->channel_bits[(size_t)h * nb + q];
+          if (w != 4 && w != 8) return QSTATE_E_INVALID;
+          // a value-axis scale group never mixes widths
+          if (c->group_axis == QSTATE_VALUE_AXIS && c->group > 16 && c->group % 16 == 0 &&
+              q % (c->group / 16) != 0 && w != c->channel_bits[(size_t)h * nb + q - 1])
+            return QSTATE_E_INVALID;
+        }
+    }
   }
   if (c->dk != 64 && c->dk != 128 && c->dk != 256) return QSTATE_E_UNSUPPORTED;
   if (c->heads > kMaxHeads || c->dv > kMaxDv) return QSTATE_E_UNSUPPORTED;
@@ -71,10 +97,8 @@ void layout(const qstate_config* c, size_t* codes_bytes, size_t* scales_bytes, u
     return;
   }
   uint64_t pb = 0;
-  for (int h = 0; h < c->heads; ++h) {
-    const int bits = c->head_bits ? c->head_bits[h] : 8;
-    pb += (uint64_t)c->dv * c->dk * bits / 8;
-  }
+  for (int h = 0; h < c->heads; ++h)
+    for (int q = 0; q < c->dk / 16; ++q) pb += (uint64_t)c->dv * 2 * block_width(c, h, q);
   *codes_bytes = (size_t)pb * c->batch;
   const size_t per_head = c->group_axis == QSTATE_KEY_AXIS
                               ? (size_t)(c->dv / c->group) * c->dk
@@ -112,8 +136,8 @@ qs::KParams base_params(const qstate* s) {
   p.slice_rows = unit_rows * units_per_slice;
   p.slices = (units + units_per_slice - 1) / units_per_slice;
   p.bytes_per_b = s->bytes_per_b;
-  p.head_bytes4 = (uint32_t)((uint64_t)s->cfg.dv * s->cfg.dk / 2);
-  std::memcpy(p.int8_mask, s->int8_mask, sizeof(p.int8_mask));
+  std::memcpy(p.int8_blocks, s->int8_blocks, sizeof(p.int8_blocks));
+  std::memcpy(p.head_units, s->head_units, sizeof(p.head_units));
   p.seed = s->cfg.seed;
   p.layer = s->cfg.layer;
   p.step = s->step;
@@ -150,11 +174,18 @@ int qstate_create(const qstate_config* cfg, void* codes_dev, void* scales_dev, q
   if (!s) return QSTATE_E_NOMEM;
   std::memset(s, 0, sizeof(*s));
   s->cfg = *cfg;
-  for (int h = 0; h < cfg->heads; ++h) {
-    s->bits[h] = cfg->fp32_state ? 32 : (cfg->head_bits ? cfg->head_bits[h] : 8);
-    if (s->bits[h] == 8) s->int8_mask[h >> 5] |= 1u << (h & 31);
+  if (!cfg->fp32_state) {
+    // head (b, h) starts at b * bytes_per_b + 8 dv * head_units[h]: a row
+    // of head h takes 8 bytes per INT4 block and 16 per INT8 block
+    uint32_t units = 0;
+    for (int h = 0; h < cfg->heads; ++h) {
+      s->int8_blocks[h] = int8_blocks(cfg, h);
+      s->head_units[h] = units;
+      units += (uint32_t)(cfg->dk / 16 + __builtin_popcount(s->int8_blocks[h]));
+    }
   }
   s->cfg.head_bits = nullptr;
+  s->cfg.channel_bits = nullptr;
   size_t cb = 0, sb = 0;
   qstate_config tmp = *cfg;
   layout(&tmp, &cb, &sb, &s->bytes_per_b);

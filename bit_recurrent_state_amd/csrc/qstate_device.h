@@ -330,20 +330,113 @@ __device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t ke
 }
 
 // ---------------------------------------------------------------------------
+// Widths chosen per lane at run time (heads with per-channel bits): one
+// lane's 16 codes are INT8 (four words) or INT4 (two words).  The rounding
+// arithmetic is shared; only widening and packing depend on the width.
+// ---------------------------------------------------------------------------
+
+// Offset-binary floats cu = c + 2^(n-1) of 16 codes; INT4 nibbles are first
+// widened to bytes in element order, so one set of byte conversions serves
+// both widths.
+__device__ __forceinline__ void unpack16_rt(const uint32_t* w, bool is8, float* cu) {
+  uint32_t b[4];
+  if (is8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = w[q] ^ 0x80808080u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t x = w[q] ^ 0x88888888u;
+      const uint32_t lo = x & 0x0F0F0F0Fu;         // even elements of the word
+      const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // odd elements
+      b[2 * q] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+      b[2 * q + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) cu[4 * q + p] = (float)((b[q] >> (8 * p)) & 0xFFu);
+}
+
+// group_scale with r = 127 (INT8) or 7 (INT4) chosen at run time; the same
+// operations and constants as group_scale<R>.
+__device__ __forceinline__ void group_scale_rt(float m, bool is8, float& s, float& inv) {
+  const float r = is8 ? 127.0f : 7.0f;
+  const float c = is8 ? 1.0f / 127.0f : 1.0f / 7.0f;
+  const float q = m * c;
+  s = __builtin_fmaf(__builtin_fmaf(-q, r, m), c, q);
+  if (__builtin_expect(m < 0x1p-100f && m != 0.0f, 0)) s = m / r;
+  float v = r / m;
+  if (__builtin_fmaf(m, v, -r) > 0.0f) v = __int_as_float(__float_as_int(v) - 1);
+  inv = (m == 0.0f) ? 0.0f : v;
+}
+
+// Requantize 16 elements; the same rounding as quantize16 with the lane's
+// width chosen at run time.  inv16/s_old16/s_new16: one inverse scale and
+// old/new scale per element (key-axis groups) or the lane's group values
+// repeated (value-axis groups).
+template <int RND>
+__device__ __forceinline__ void quantize16_rt(const float* sp, const float* inv16, uint32_t key,
+                                              uint32_t block, const uint32_t* wprev,
+                                              const float* s_old16, const float* s_new16,
+                                              bool is8, uint32_t* out) {
+  uint32_t src[16];
+  if constexpr (RND == kSR) {
+    float R[16];
+    block_r16(key, block, R);
+    float imax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) imax = fmaxf(imax, inv16[j]);
+    if (__builtin_expect(imax <= 0x1p100f, 1)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j] * 65536.0f, R[j]));
+    } else {  // a tiny-magnitude group, where inv * 2^16 could overflow
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j], R[j] * (1.0f / 65536.0f)))
+                 << 16;
+    }
+  } else {
+    constexpr float kMagic = 12582912.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv16[j], kMagic));
+    if constexpr (RND == kBDR) {
+      const float r = is8 ? 127.0f : 7.0f;
+      const float bias = is8 ? 128.0f : 8.0f;
+      float prev[16];
+      unpack16_rt(wprev, is8, prev);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = __builtin_fmaf(prev[j], s_old16[j], -bias * s_old16[j]);
+        float y = __uint_as_float(src[j]);
+        const float st = (y - kMagic) * s_new16[j];
+        const float x = sp[j];
+        if (x > pv && st < pv) y += 1.0f;
+        if (x < pv && st > pv) y -= 1.0f;
+        y = fminf(fmaxf(y, kMagic - r), kMagic + r);
+        src[j] = __float_as_uint(y);
+      }
+    }
+  }
+  constexpr int BP = RND == kSR ? 2 : 0;
+  if (is8) {
+    pack16<8, BP>(src, out);
+  } else {
+    pack16<4, BP>(src, out);
+    out[2] = out[3] = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Per-head geometry.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ bool head_is_int8(const KParams& p, int h) {
-  return (p.int8_mask[h >> 5] >> (h & 31)) & 1u;
-}
-
-// Byte offset of head (b, h): b * bytes_per_b + sum_{h' < h} bytes(h'), an
-// INT8 head being twice an INT4 head.
+// Byte offset of head (b, h): b * bytes_per_b + 8 dv * head_units[h], where
+// head_units counts the 8-byte units of the rows of the heads before h.
 __device__ __forceinline__ uint64_t head_code_offset(const KParams& p, int b, int h) {
-  uint32_t n8 = 0;
-  for (int w = 0; w < (h >> 5); ++w) n8 += __popc(p.int8_mask[w]);
-  if (h & 31) n8 += __popc(p.int8_mask[h >> 5] & ((1u << (h & 31)) - 1u));
-  return (uint64_t)b * p.bytes_per_b + (uint64_t)(h + n8) * p.head_bytes4;
+  return (uint64_t)b * p.bytes_per_b + (uint64_t)8 * p.dv * p.head_units[h];
 }
 
 template <int N>

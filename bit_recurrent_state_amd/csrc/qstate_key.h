@@ -93,19 +93,38 @@ __device__ __forceinline__ void lds_load(const float* ptr, float (&x)[N]) {
   }
 }
 
+// Code placement of a lane's 16-column block in a row.  BITS = 8 or 4: a
+// head of one width (compile-time); BITS = 0: widths per block from the
+// head's INT8-block mask, a row holding 16 bytes per INT8 block and 8 per
+// INT4 block in column order.
+template <int DK, int BITS>
+struct LaneCodes {
+  bool is8;        // this lane's block stores INT8 codes
+  int row_bytes;   // bytes of one row of the head
+  int lane_off;    // byte offset of the lane's block inside a row
+  __device__ __forceinline__ LaneCodes(uint32_t mask, int lr) {
+    constexpr int LPR = DK / 16;
+    if constexpr (BITS != 0) {
+      is8 = BITS == 8;
+      row_bytes = DK * BITS / 8;
+      lane_off = lr * 2 * BITS;
+    } else {
+      is8 = (mask >> lr) & 1u;
+      row_bytes = 8 * (LPR + __popc(mask));
+      lane_off = 8 * (lr + __popc(mask & ((1u << lr) - 1u)));
+    }
+  }
+};
+
 // Step (OP = kStep) or import (OP = kImport) of a quantized head with
 // key-axis groups.  LDS: partial column maxima, old scales, new scales and
-// inverse scales of the block's row groups.
+// inverse scales of the block's row groups.  BITS = 0: mixed widths.
 template <int OP, int MIXER, int RND, int DK, int BITS, int G>
 __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl, float* lds) {
   using K = KGeo<DK, G>;
   constexpr int E = K::E, LPR = K::LPR, RPW = K::RPW, NI = K::NI, RB = K::RB, NW = K::NW;
   constexpr int BR = K::BR, LG = K::LG, PARTS = K::PARTS;
-  constexpr int R = (1 << (BITS - 1)) - 1;
-  constexpr float bias = (float)(1 << (BITS - 1));
-  constexpr int ROW_BYTES = DK * BITS / 8;
-  constexpr int LANE_BYTES = E * BITS / 8;  // 16 (INT8) or 8 (INT4)
-  constexpr int NWORDS = LANE_BYTES / 4;
+  const uint32_t mask = p.int8_blocks[sl.h];
   float* pm = lds;                        // [LG][PARTS][DK]
   float* so = pm + LG * PARTS * DK;       // [LG][DK] scales before the step
   float* sn = so + LG * DK;               // [LG][DK] new scales
@@ -117,6 +136,8 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   const int lr = lane % LPR;
   const int rsub = lane / LPR;
   const int col0 = lr * E;
+  const LaneCodes<DK, BITS> lc(mask, lr);
+  const float bias = lc.is8 ? 128.0f : 8.0f;
   uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
   float* hscales = p.scales + (size_t)sl.head * (p.dv / G) * DK;
   const uint32_t key =
@@ -159,8 +180,8 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     for (int it = 0; it < NI; ++it) {
       const int row = min(base + wv * RB + it * RPW + rsub, p.dv - 1);
       if constexpr (OP == kStep) {
-        const uint8_t* src = hcodes + (size_t)row * ROW_BYTES + lr * LANE_BYTES;
-        if constexpr (NWORDS == 4) {
+        const uint8_t* src = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
+        if (lc.is8) {
           const uint4 t = *reinterpret_cast<const uint4*>(src);
           wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = t.z, wc[it][3] = t.w;
         } else {
@@ -186,7 +207,10 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
         float sc[E];
         lds_load(so + lg * DK + col0, sc);
         float d[E];
-        unpack16<BITS>(wc[it], d);
+        if constexpr (BITS != 0)
+          unpack16<BITS>(wc[it], d);
+        else
+          unpack16_rt(wc[it], lc.is8, d);
         if constexpr (vector_decay(MIXER)) {
 #pragma unroll
           for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], sc[j], -bias * sc[j]) * al[j];
@@ -231,7 +255,10 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
 #pragma unroll 8
       for (int q = 0; q < PARTS; ++q) m = fmaxf(m, pm[((size_t)lg * PARTS + q) * DK + j]);
       float s, inv;
-      group_scale<R>(m, s, inv);
+      if constexpr (BITS != 0)
+        group_scale<(1 << (BITS - 1)) - 1>(m, s, inv);
+      else
+        group_scale_rt(m, (mask >> (j / 16)) & 1u, s, inv);
       sn[t] = s;
       si[t] = inv;
       const int grow = base / G + lg;
@@ -252,11 +279,14 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       }
       uint32_t out[4];
       const uint32_t block = (uint32_t)((row * DK + col0) >> 4);
-      quantize16_cols<BITS, (OP == kImport && RND == kBDR) ? kRTN : RND>(
-          sp[it], inv16, key, block, wc[it], s_old, s_new, out);
+      constexpr int QR = (OP == kImport && RND == kBDR) ? kRTN : RND;
+      if constexpr (BITS != 0)
+        quantize16_cols<BITS, QR>(sp[it], inv16, key, block, wc[it], s_old, s_new, out);
+      else
+        quantize16_rt<QR>(sp[it], inv16, key, block, wc[it], s_old, s_new, lc.is8, out);
       if (row < p.dv) {
-        uint8_t* dst = hcodes + (size_t)row * ROW_BYTES + lr * LANE_BYTES;
-        if constexpr (NWORDS == 4)
+        uint8_t* dst = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
+        if (lc.is8)
           *reinterpret_cast<uint4*>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
         else
           *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
@@ -271,13 +301,12 @@ template <int OP, int DK, int BITS, int G>
 __device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
   using K = KGeo<DK, G>;
   constexpr int E = K::E, LPR = K::LPR, RPW = K::RPW, NW = K::NW;
-  constexpr float bias = (float)(1 << (BITS - 1));
-  constexpr int ROW_BYTES = DK * BITS / 8;
-  constexpr int LANE_BYTES = E * BITS / 8;
   const int tid = threadIdx.x;
   const int lane = tid % 64;
   const int lr = lane % LPR;
   const int col0 = lr * E;
+  const LaneCodes<DK, BITS> lc(p.int8_blocks[sl.h], lr);
+  const float bias = lc.is8 ? 128.0f : 8.0f;
   const uint8_t* hcodes =
       reinterpret_cast<const uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
   const float* hscales = p.scales + (size_t)sl.head * (p.dv / G) * DK;
@@ -289,8 +318,8 @@ __device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
     const bool ok = row < sl.r1;
     const int rr = min(row, p.dv - 1);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
-    const uint8_t* src = hcodes + (size_t)rr * ROW_BYTES + lr * LANE_BYTES;
-    if constexpr (LANE_BYTES == 16) {
+    const uint8_t* src = hcodes + (size_t)rr * lc.row_bytes + lc.lane_off;
+    if (lc.is8) {
       const uint4 t = *reinterpret_cast<const uint4*>(src);
       w[0] = t.x, w[1] = t.y, w[2] = t.z, w[3] = t.w;
     } else {
@@ -299,7 +328,10 @@ __device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
     }
     float sc[E], d[E];
     loadv(hscales + (size_t)(rr / G) * DK + col0, sc);
-    unpack16<BITS>(w, d);
+    if constexpr (BITS != 0)
+      unpack16<BITS>(w, d);
+    else
+      unpack16_rt(w, lc.is8, d);
 #pragma unroll
     for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], sc[j], -bias * sc[j]);
     if constexpr (OP == kExport) {
@@ -320,19 +352,25 @@ __global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_kernel(const KPara
   using K = KGeo<DK, G>;
   __shared__ float lds[K::LG * (K::PARTS + 3) * DK];
   const Slice sl = wave_slice(p);
-  if (head_is_int8(p, sl.h))
+  const uint32_t m = p.int8_blocks[sl.h];
+  if (m == (1u << (DK / 16)) - 1u)
     key_quant_head<OP, MIXER, RND, DK, 8, G>(p, sl, lds);
-  else
+  else if (m == 0u)
     key_quant_head<OP, MIXER, RND, DK, 4, G>(p, sl, lds);
+  else
+    key_quant_head<OP, MIXER, RND, DK, 0, G>(p, sl, lds);
 }
 
 template <int OP, int DK, int G>
 __global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_aux_kernel(const KParams p) {
   const Slice sl = wave_slice(p);
-  if (head_is_int8(p, sl.h))
+  const uint32_t m = p.int8_blocks[sl.h];
+  if (m == (1u << (DK / 16)) - 1u)
     key_aux_head<OP, DK, 8, G>(p, sl);
-  else
+  else if (m == 0u)
     key_aux_head<OP, DK, 4, G>(p, sl);
+  else
+    key_aux_head<OP, DK, 0, G>(p, sl);
 }
 
 // FP32-state readout: o = S q.

@@ -25,9 +25,9 @@ struct KParams {
   int32_t slices;        // workgroups per head (row slices); the grid is B*H*slices
   int32_t slice_rows;    // rows per slice: a multiple of 32 (value axis) or of
                          // the key-axis block rows max(G, 4096/dk)
-  uint64_t bytes_per_b;  // code bytes of one batch row (all heads)
-  uint32_t head_bytes4;  // code bytes of an INT4 head = dv*dk/2
-  uint32_t int8_mask[8]; // bit h set: head h stores INT8 codes
+  uint64_t bytes_per_b;        // code bytes of one batch row (all heads)
+  uint16_t int8_blocks[256];   // per head: bit q set = 16-column block q is INT8
+  uint32_t head_units[256];    // per head: byte offset in a batch row / (8 dv)
   uint64_t seed;
   uint32_t layer;
   uint64_t step;         // stochastic-rounding counter of this event

@@ -296,16 +296,220 @@ __device__ __forceinline__ void aux_quant_head(const KParams& p, const Slice sl)
 }
 
 // ---------------------------------------------------------------------------
+// Heads whose 16-column blocks have different widths (per-channel bits,
+// LoReS 2/4).  Every lane owns the 16 columns of one block, 16 bytes of INT8
+// or 8 bytes of INT4 codes, so a row spans dk/16 lanes whatever the widths;
+// the block starts 8 * (q + INT8 blocks before q) bytes into its row.  A
+// value-axis group covers G/16 lanes of one width (checked at create).  The
+// loads follow the same prefetch ring as the uniform heads: every lane loads
+// two 8-byte halves, an INT4 lane reading its one half twice, so the loads
+// stay unconditional.
+// ---------------------------------------------------------------------------
+
+struct MixedLane {
+  bool is8;
+  int row_bytes, lane_off;
+  __device__ __forceinline__ MixedLane(uint32_t mask, int lr, int lpr) {
+    is8 = (mask >> lr) & 1u;
+    row_bytes = 8 * (lpr + __popc(mask));
+    lane_off = 8 * (lr + __popc(mask & ((1u << lr) - 1u)));
+  }
+};
+
+struct RowMixed {
+  uint2 a, b;  // codes: bytes 0..7 and 8..15 of an INT8 block; an INT4 block in a
+  float s, v;
+};
+
+__device__ __forceinline__ void store_block(uint8_t* dst, bool is8, const uint32_t (&w)[4]) {
+  if (is8)
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  else
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+}
+
+// Group absmax over the G/16 lanes of the lane's group, scale, and the
+// lane's 16 codes.
+template <int RND, int LPG>
+__device__ __forceinline__ void quantize_block(const float (&sp)[16], bool is8, uint32_t key,
+                                               uint32_t block, const uint32_t (&wprev)[4],
+                                               float s_old, float& s_new, uint32_t (&out)[4]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(sp[j]));
+  m = lanes_max<LPG>(m);
+  float inv;
+  group_scale_rt(m, is8, s_new, inv);
+  float inv16[16], so16[16], sn16[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) inv16[j] = inv, so16[j] = s_old, sn16[j] = s_new;
+  quantize16_rt<RND>(sp, inv16, key, block, wprev, so16, sn16, is8, out);
+}
+
+template <int MIXER, int RND, int DK, int G>
+__device__ __forceinline__ void step_mixed_head(const KParams& p, const Slice sl) {
+  constexpr int E = 16, LPR = DK / 16, RPW = 64 / LPR, LPG = G / 16;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = col0 / G;
+  const MixedLane ml(p.int8_blocks[sl.h], lr, LPR);
+  const float bias = ml.is8 ? 128.0f : 8.0f;
+  const int half2 = ml.is8 ? 8 : 0;  // offset of the second 8-byte load
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const float* vh = p.v + (size_t)sl.head * p.dv;
+  float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
+
+  const uint32_t key = RND == kSR ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  float alpha_s = 0.0f, beta = 0.0f;
+  if constexpr (vector_decay(MIXER)) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+    alpha_s = p.alpha[sl.head];
+  }
+  if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
+
+  auto load = [&](int it) {  // in-range rows only (clamped); stored only if real
+    RowMixed in;
+    const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
+    const uint8_t* src = hcodes + (size_t)row * ml.row_bytes + ml.lane_off;
+    in.a = *reinterpret_cast<const uint2*>(src);
+    in.b = *reinterpret_cast<const uint2*>(src + half2);
+    in.s = hscales[(size_t)row * ngr + gcol];
+    in.v = vh[row];
+    return in;
+  };
+  RowMixed ring[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    ring[k] = load(k);
+    asm volatile("" ::: "memory");
+  }
+  const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
+  for (int t = 0; t < n_trips; ++t) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int it = t * kPrefetch + k;
+      const int row = sl.r0 + it * RPW + rsub;
+      const bool store_ok = it < n_it && row < sl.r1;
+      const uint32_t w[4] = {ring[k].a.x, ring[k].a.y, ring[k].b.x, ring[k].b.y};
+      const float s_old = ring[k].s, vrow = ring[k].v;
+      float d[E];
+      unpack16_rt(w, ml.is8, d);
+      if constexpr (vector_decay(MIXER)) {
+        const float nb = -bias * s_old;
+#pragma unroll
+        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], s_old, nb) * al[j];
+      } else {
+        const float sa = s_old * alpha_s, nb = -bias * sa;
+#pragma unroll
+        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], sa, nb);
+      }
+      float wt;
+      if constexpr (delta_rule(MIXER)) {
+        const float u = row_sum<LPR>(lane_dot(d, kk));
+        wt = beta * (vrow - u);
+      } else if constexpr (MIXER == kGLA) {
+        wt = vrow;
+      } else {
+        wt = beta * vrow;
+      }
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
+      const float o = row_sum<LPR>(lane_dot(d, qq));
+      float s_new;
+      uint32_t out[4];
+      quantize_block<RND, LPG>(d, ml.is8, key, (uint32_t)((row * DK + col0) >> 4), w, s_old,
+                               s_new, out);
+      if (store_ok) {
+        store_block(hcodes + (size_t)row * ml.row_bytes + ml.lane_off, ml.is8, out);
+        if (lr % LPG == 0) hscales[(size_t)row * ngr + gcol] = s_new;
+        if (oh && lr == 0) oh[row] = o;
+      }
+    }
+  }
+}
+
+// Import, export and readout of a mixed-width head.
+template <int OP, bool SR, int DK, int G>
+__device__ __forceinline__ void aux_mixed_head(const KParams& p, const Slice sl) {
+  constexpr int E = 16, LPR = DK / 16, RPW = 64 / LPR, LPG = G / 16;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = col0 / G;
+  const MixedLane ml(p.int8_blocks[sl.h], lr, LPR);
+  const float bias = ml.is8 ? 128.0f : 8.0f;
+  const int half2 = ml.is8 ? 8 : 0;
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const size_t hoff = (size_t)sl.head * p.dv * DK;
+  const uint32_t key = (OP == kImport && SR) ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float qq[E];
+  if constexpr (OP == kReadout) loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  for (int rbase = sl.r0; rbase < sl.r1; rbase += RPW) {
+    const int row = rbase + rsub;
+    const bool ok = row < sl.r1;
+    const int rr = min(row, sl.r1 - 1);
+    uint8_t* codes = hcodes + (size_t)rr * ml.row_bytes + ml.lane_off;
+    if constexpr (OP == kImport) {
+      float x[E];
+      loadv(p.src + hoff + (size_t)rr * DK + col0, x);
+      const uint32_t no_prev[4] = {0u, 0u, 0u, 0u};  // read only by BDR, never on import
+      float s_new;
+      uint32_t out[4];
+      quantize_block<SR ? kSR : kRTN, LPG>(x, ml.is8, key, (uint32_t)((row * DK + col0) >> 4),
+                                           no_prev, 0.0f, s_new, out);
+      if (ok) {
+        store_block(codes, ml.is8, out);
+        if (lr % LPG == 0) hscales[(size_t)row * ngr + gcol] = s_new;
+      }
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2*>(codes);
+      const uint2 b = *reinterpret_cast<const uint2*>(codes + half2);
+      const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+      const float s = hscales[(size_t)rr * ngr + gcol];
+      float d[E];
+      unpack16_rt(w, ml.is8, d);
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], s, -bias * s);
+      if constexpr (OP == kExport) {
+        if (ok) storev(p.dst + hoff + (size_t)row * DK + col0, d);
+      } else {
+        const float o = row_sum<LPR>(lane_dot(d, qq));
+        if (ok && lr == 0) p.o[(size_t)sl.head * p.dv + row] = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Kernels and dispatch.
 // ---------------------------------------------------------------------------
 
 template <int MIXER, int RND, int DK, int G>
 __global__ __launch_bounds__(kThreads) void step_kernel(const KParams p) {
   const Slice sl = wave_slice(p);
-  if (head_is_int8(p, sl.h))
+  const uint32_t m = p.int8_blocks[sl.h];
+  if (m == (1u << (DK / 16)) - 1u)
     step_quant_head<MIXER, RND, DK, 8, G>(p, sl);
-  else
+  else if (m == 0u)
     step_quant_head<MIXER, RND, DK, 4, G>(p, sl);
+  else
+    step_mixed_head<MIXER, RND, DK, G>(p, sl);
 }
 
 template <int MIXER, int DK>
@@ -316,10 +520,13 @@ __global__ __launch_bounds__(kThreads) void step_fp32_kernel(const KParams p) {
 template <int OP, bool SR, int DK, int G>
 __global__ __launch_bounds__(kThreads) void aux_kernel(const KParams p) {
   const Slice sl = wave_slice(p);
-  if (head_is_int8(p, sl.h))
+  const uint32_t m = p.int8_blocks[sl.h];
+  if (m == (1u << (DK / 16)) - 1u)
     aux_quant_head<OP, SR, DK, 8, G>(p, sl);
-  else
+  else if (m == 0u)
     aux_quant_head<OP, SR, DK, 4, G>(p, sl);
+  else
+    aux_mixed_head<OP, SR, DK, G>(p, sl);
 }
 
 template <int DK>

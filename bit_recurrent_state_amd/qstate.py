@@ -39,25 +39,38 @@ class Config:
     seed: int = 0
     layer: int = 0
     group_axis: int = VALUE_AXIS
+    channel_bits: Optional[Sequence[Sequence[int]]] = None  # [heads][dk/16], overrides head_bits
 
     def to_c(self):
-        """(QStateConfig, keep-alive buffer)."""
-        hb = None
-        ptr = None
+        """(QStateConfig, keep-alive buffers)."""
+        keep = []
+        ptr = cptr = None
         if self.head_bits is not None:
             hb = (ctypes.c_uint8 * self.heads)(*[int(x) for x in self.head_bits])
             ptr = ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8))
+            keep.append(hb)
+        if self.channel_bits is not None:
+            flat = np.asarray(self.channel_bits, np.uint8).reshape(-1)
+            if flat.size != self.heads * (self.dk // 16):
+                raise ValueError("channel_bits: expected [heads][dk/16] widths")
+            cb = (ctypes.c_uint8 * flat.size)(*[int(x) for x in flat])
+            cptr = ctypes.cast(cb, ctypes.POINTER(ctypes.c_uint8))
+            keep.append(cb)
         c = QStateConfig(self.batch, self.heads, self.dk, self.dv, self.group, self.mixer,
                          self.rounding, int(bool(self.fp32_state)), ptr, self.seed, self.layer,
-                         self.group_axis)
-        return c, hb
+                         self.group_axis, cptr)
+        return c, keep
 
     def bits(self) -> np.ndarray:
+        """Widths per head and 16-column block, [heads][dk/16] (32 for an FP32 state)."""
+        nb = self.dk // 16
         if self.fp32_state:
-            return np.full(self.heads, 32, np.int64)
+            return np.full((self.heads, nb), 32, np.int64)
+        if self.channel_bits is not None:
+            return np.asarray(self.channel_bits, np.int64).reshape(self.heads, nb)
         if self.head_bits is None:
-            return np.full(self.heads, 8, np.int64)
-        return np.asarray(self.head_bits, np.int64)
+            return np.full((self.heads, nb), 8, np.int64)
+        return np.repeat(np.asarray(self.head_bits, np.int64)[:, None], nb, axis=1)
 
 
 def _stream(stream) -> ctypes.c_void_p:

@@ -80,10 +80,13 @@
  *   alpha           float [B][H]      (GDN, SCALAR)  or  [B][H][dk] (GLA, KDA)
  *   beta            float [B][H]      (GDN, KDA: beta, SCALAR: dt; GLA: unused)
  *   codes           heads in (b, h) order; head (b,h) starts at byte
- *                   b*P + sum_{h'<h} dv*dk*n_{h'}/8, P = sum_h dv*dk*n_h/8.
- *                   Row-major [dv][dk] inside a head.  INT8: int8 two's
- *                   complement.  INT4: two's-complement nibbles, byte
- *                   (i*dk + j)/2 holds even j in bits 0..3, odd j in 4..7.
+ *                   b*P + sum_{h'<h} dv*R_{h'}, P = sum_h dv*R_h, where R_h
+ *                   is a row's bytes: 16 per INT8 and 8 per INT4 block of
+ *                   16 key columns (dk*n_h/8 for a head of one width n_h).
+ *                   Rows follow each other inside a head; a row holds its
+ *                   blocks in column order.  INT8: int8 two's complement.
+ *                   INT4: two's-complement nibbles, within a block byte t/2
+ *                   holds even column t in bits 0..3, odd t in bits 4..7.
  *   scales          float [B][H][dv][dk/G] (value axis) or [B][H][dv/G][dk]
  *                   (key axis)
  *   FP32 state      float [B][H][dv][dk]  (fp32_state = 1)
@@ -155,6 +158,12 @@ typedef struct {
   uint64_t seed;            /* stochastic-rounding key                        */
   uint32_t layer;           /* stochastic-rounding key                        */
   int32_t group_axis;       /* qstate_group_axis; 0 = value axis (default)    */
+  const uint8_t* channel_bits; /* host [heads][dk/16] or NULL: the width (4 or 8)
+                               of each block of 16 key columns, overriding
+                               head_bits (LoReS 2/4: more bits for the
+                               slowest-decaying channels; order channels so
+                               that slow ones share blocks).  Value-axis
+                               groups may not mix widths.  Copied at create. */
 } qstate_config;
 
 typedef struct qstate qstate; /* opaque; host-side metadata only */
@@ -199,9 +208,10 @@ int qstate_destroy(qstate* h);
 /* Static message for a status code. */
 const char* qstate_strerror(int status);
 
-/* Decay-based per-head bit allocation ("allocate more bits to the slowest-
- * decaying heads", LoReS 2/4).  retention[h] is larger for slower decay
- * (e.g. alpha_h, or exp(-softplus(A_h))).
+/* Decay-based bit allocation (LoReS 2/4: more bits for the slowest-decaying
+ * heads or channels).  retention[h] is larger for slower decay (e.g. alpha_h,
+ * exp(-softplus(A_h)), or the mean retention of a group of key channels when
+ * allocating channel_bits); `heads` is the number of entries.
  *   mode 0: out[h] = hi if retention[h] > thr_or_frac else lo
  *   mode 1: the round(thr_or_frac * heads) heads with the largest retention
  *           get hi (ties: the lower head index first), the rest lo. */

@@ -58,6 +58,22 @@ def head_bits(w: W.Workload, seed=0, layer=0):
     return lib_bits
 
 
+def block_bits(w: W.Workload, seed=0, layer=0):
+    """Widths per head and 16-column block [H][dk/16].  "channel_half": per head
+    the slower half of the G-channel groups INT8 (same rank rule, applied to
+    the groups' mean channel retention), else the per-head widths."""
+    nb = w.dk // 16
+    if w.bits_policy != "channel_half":
+        return np.repeat(head_bits(w, seed, layer)[:, None], nb, axis=1)
+    ret = W.group_retention(w, seed, layer)
+    out = np.empty((w.H, nb), np.uint8)
+    for h in range(w.H):
+        lib_bits = Q.qstate_bits_by_decay(ret[h], 1, 0.5)
+        assert np.array_equal(lib_bits, oracle.bits_by_decay(ret[h], 1, 0.5))
+        out[h] = np.repeat(lib_bits, w.G // 16)  # groups of G channels, G/16 blocks each
+    return out
+
+
 @dataclass
 class Report:
     steps: int = 0
@@ -92,12 +108,17 @@ class Run:
         self.w = w
         self.rounding = w.rounding if rounding is None else rounding
         self.seed, self.layer = seed, layer
+        nb = w.dk // 16
         if head_bits_override is not None:
-            self.hb = np.asarray(head_bits_override, np.uint8)
+            hb = np.asarray(head_bits_override, np.uint8)
+            self.bb = hb if hb.ndim == 2 else np.repeat(hb[:, None], nb, axis=1)
         else:
-            self.hb = head_bits(w, seed, layer)
+            self.bb = block_bits(w, seed, layer)
+        self.hb = self.bb.max(axis=1)  # widest block per head (reporting only)
+        uniform = bool(np.all(self.bb == self.bb[:, :1]))
         self.cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, False,
-                            [int(x) for x in self.hb], seed, layer, w.axis)
+                            [int(x) for x in self.bb[:, 0]] if uniform else None, seed, layer,
+                            w.axis, None if uniform else self.bb.tolist())
         self.ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, seed, layer,
                                w.axis)
         all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
@@ -111,8 +132,8 @@ class Run:
         return W.step_inputs(self.w, t, self.seed, self.layer)
 
     def head_codes_slice(self, b, h):
-        off = oracle.head_offset(self.ocfg, b, h, self.hb)
-        n = self.w.dv * self.w.dk * int(self.hb[h]) // 8
+        off = oracle.head_offset(self.ocfg, b, h, self.bb)
+        n = oracle.head_code_bytes(self.ocfg, self.bb[h])
         return off, n
 
     def _alpha_head(self, alpha, b, h):
@@ -154,7 +175,7 @@ class Run:
         self.gpu.load_fp32(S_gpu)  # counter 0 -> 1
         self.ref, xvals = {}, {}
         for (b, h) in self.heads:
-            codes, scales, xv = oracle.head_quantize(self.ocfg, b, h, int(self.hb[h]),
+            codes, scales, xv = oracle.head_quantize(self.ocfg, b, h, self.bb[h],
                                                      S_ref[(b, h)], 0, want_xval=True)
             self.ref[(b, h)] = (codes, scales)
             xvals[(b, h)] = xv
@@ -172,7 +193,7 @@ class Run:
         o_ref, xvals = {}, {}
         for (b, h) in self.heads:
             codes, scales = self.ref[(b, h)]
-            o, _, xv = oracle.head_step(self.ocfg, b, h, int(self.hb[h]), codes, scales, q[b, h],
+            o, _, xv = oracle.head_step(self.ocfg, b, h, self.bb[h], codes, scales, q[b, h],
                                         k[b, h], v[b, h], self._alpha_head(alpha, b, h),
                                         self._beta_head(beta, b, h), counter, want_xval=True)
             o_ref[(b, h)] = o
@@ -188,7 +209,7 @@ class Run:
         codes_g = _to_np(self.gpu.codes)
         scales_g = _to_np(self.gpu.scales).reshape(w.B, w.H, -1)
         for (b, h) in self.heads:
-            bits = int(self.hb[h])
+            bits = self.bb[h]
             off, n = self.head_codes_slice(b, h)
             cg = codes_g[off:off + n]
             cr, sr = self.ref[(b, h)]
@@ -210,8 +231,8 @@ class Run:
 
     def _exempt_or_fail(self, step, b, h, bits, cg, cr, xvals):
         w = self.w
-        a = _decode(cg, bits)
-        r = _decode(cr, bits)
+        a = _decode(cg, bits, w.dv, w.dk)
+        r = _decode(cr, bits, w.dv, w.dk)
         bad = np.nonzero(a != r)[0]
         x = xvals[(b, h)].ravel()[bad]
         if self.rounding == W.SR:
@@ -243,9 +264,9 @@ class Run:
         og = _to_np(o).reshape(w.B, w.H, w.dv)
         for (b, h) in self.heads:
             codes, scales = self.ref[(b, h)]
-            Sr = oracle.head_dequantize(self.ocfg, int(self.hb[h]), codes, scales)
+            Sr = oracle.head_dequantize(self.ocfg, self.bb[h], codes, scales)
             assert np.array_equal(Sg[b, h], Sr), f"export differs at head {(b, h)}"
-            orr = oracle.head_readout(self.ocfg, int(self.hb[h]), codes, scales, q[b, h])
+            orr = oracle.head_readout(self.ocfg, self.bb[h], codes, scales, q[b, h])
             ok, err = _close(og[b, h], orr)
             assert ok, f"readout differs at head {(b, h)}: {err}"
             self.rep.max_s_err = max(self.rep.max_s_err, float(np.abs(Sg[b, h] - Sr).max()))
@@ -255,11 +276,22 @@ class Run:
             self.gpu.close()
 
 
-def _decode(codes: np.ndarray, bits: int) -> np.ndarray:
-    if bits == 8:
-        return codes.view(np.int8).astype(np.int32)
-    x = np.empty(codes.size * 2, np.int32)
-    x[0::2] = codes & 0xF
-    x[1::2] = codes >> 4
-    x[x >= 8] -= 16
-    return x
+def _decode(codes: np.ndarray, bb: np.ndarray, dv: int, dk: int) -> np.ndarray:
+    """Codes of one head in element order (i*dk + j), from per-block widths."""
+    bb = np.asarray(bb).reshape(-1)
+    row_bytes = int(np.sum(2 * bb.astype(np.int64)))
+    rows = codes.reshape(dv, row_bytes)
+    out = np.empty((dv, dk), np.int32)
+    off = 0
+    for q, bits in enumerate(bb):
+        if bits == 8:
+            out[:, 16 * q:16 * q + 16] = rows[:, off:off + 16].view(np.int8)
+            off += 16
+        else:
+            blk = rows[:, off:off + 8]
+            x = np.empty((dv, 16), np.int32)
+            x[:, 0::2], x[:, 1::2] = blk & 0xF, blk >> 4
+            x[x >= 8] -= 16
+            out[:, 16 * q:16 * q + 16] = x
+            off += 8
+    return out.reshape(-1)

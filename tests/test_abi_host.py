@@ -59,6 +59,11 @@ def test_state_bytes(L):
     c = _cfg(fp32_state=1)
     assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
     assert cb.value == 2 * 3 * 64 * 128 * 4 and sb.value == 0
+    # per-channel widths: 16 bytes per INT8 block and 8 per INT4 block of a row
+    keepc = (ctypes.c_uint8 * 24)(*([8, 4, 4, 4, 8, 8, 4, 4] * 3))
+    c = _cfg(channel_bits=ctypes.cast(keepc, ctypes.POINTER(ctypes.c_uint8)), group=16)
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 2 * 3 * 64 * (3 * 16 + 5 * 8)
     # key-axis groups: G value rows per scale, [dv/G][dk] scales per head
     c = _cfg(head_bits=hb, group_axis=1, dk=64, dv=128, group=128)
     assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
@@ -81,6 +86,22 @@ def test_invalid_configs_rejected(L, kw, status):
     assert L.qstate_create(ctypes.byref(c), ctypes.c_void_p(4096), ctypes.c_void_p(8192),
                            ctypes.byref(h)) == status
     assert h.value is None
+
+
+def test_channel_bits_rules(L):
+    """Widths 4 or 8 only; value-axis groups may not mix widths (key-axis may)."""
+    def status(widths, **kw):
+        arr = (ctypes.c_uint8 * 24)(*widths)
+        c = _cfg(channel_bits=ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8)), **kw)
+        cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+        return L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb))
+    pairs = [8, 8, 4, 4, 8, 8, 4, 4] * 3
+    mixed = [8, 4, 4, 8, 8, 4, 4, 8] * 3
+    assert status(pairs, group=32) == 0
+    assert status(mixed, group=32) == -1
+    assert status(mixed, group=16) == 0
+    assert status(mixed, group=32, group_axis=1) == 0
+    assert status([8, 6] + [8] * 22, group=16) == -1
 
 
 def test_bad_head_bits_and_pointers(L):

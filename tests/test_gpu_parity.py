@@ -113,6 +113,41 @@ def test_key_axis_full_size_sampled_heads():
     _run(w, 2, heads=sorted((i // w.H, i % w.H) for i in idx))
 
 
+@pytest.mark.parametrize("rounding,axis", [(W.SR, 0), (W.RTN, 0), (W.BDR, 0), (W.SR, 1)])
+def test_channel_bits_every_head(rounding, axis):
+    """Per-channel widths (INT8 for the slower half of each head's 32-channel
+    groups, INT4 for the rest) on every head, both group axes."""
+    w = W.WORKLOADS[6].scaled(B=2, axis=axis)
+    from parity import block_bits
+    bb = block_bits(w)
+    assert np.any(bb == 8) and np.any(bb == 4) and not np.all(bb == bb[:, :1])
+    _run(w, 8, rounding=rounding)
+
+
+# mixed widths per 16-column block inside a head, ragged rows, every dk
+CHANNEL_RAGGED = [
+    (W.GDN, W.SR, 0, 64, 37, 16, [[8, 4, 4, 8], [4, 8, 8, 4], [4, 4, 4, 4]]),
+    (W.KDA, W.BDR, 0, 256, 45, 32, [[8, 8, 4, 4] * 4, [4, 4, 8, 8, 8, 8, 4, 4] * 2]),
+    (W.SCALAR, W.RTN, 0, 128, 70, 64, [[8] * 4 + [4] * 4, [8] * 8]),
+    (W.GLA, W.SR, 1, 128, 64, 32, [[8, 4, 8, 4, 4, 8, 4, 8], [4] * 8]),
+    (W.GDN, W.BDR, 1, 64, 128, 128, [[4, 8, 4, 8], [8, 8, 4, 4]]),
+]
+
+
+@pytest.mark.parametrize("mixer,rounding,axis,dk,dv,G,bits", CHANNEL_RAGGED)
+def test_channel_bits_shapes(mixer, rounding, axis, dk, dv, G, bits):
+    w = W.Workload(75 + mixer, f"chan_m{mixer}_dk{dk}_dv{dv}_g{G}_a{axis}", mixer, 3, len(bits),
+                   dk, dv, G, 5, 3, rounding, "int8", axis=axis)
+    _run(w, 5, hb=np.array(bits, np.uint8), seed=13)
+
+
+def test_channel_bits_full_size_sampled_heads():
+    w = W.WORKLOADS[6]
+    rng = np.random.default_rng(31)
+    idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
+    _run(w, 2, heads=sorted((i // w.H, i % w.H) for i in idx))
+
+
 @pytest.mark.parametrize("layer", [0, 5])
 def test_config4_scalar_decay_layers(layer):
     _run(W.WORKLOADS[4].scaled(B=3), 8, layer=layer)
@@ -150,7 +185,7 @@ def test_fp32_state_is_the_fp32_recurrence(mixer):
     r.warmup_and_import()
 
 
-FULL = {1: 3, 2: 2, 3: 2, 4: 2, 5: 2}
+FULL = {1: 3, 2: 2, 3: 2, 4: 2, 5: 2}  # per-channel widths (6): its own test
 
 
 @pytest.mark.parametrize("wid", sorted(FULL))

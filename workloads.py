@@ -26,7 +26,7 @@ GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR, BDR = 0, 1, 2
 
 # tensor ids for the seed sequence
-_Q, _K, _V, _BETA, _ALPHA, _HEAD_ALPHA, _HEAD_A, _DT = range(8)
+_Q, _K, _V, _BETA, _ALPHA, _HEAD_ALPHA, _HEAD_A, _DT, _CHAN_MU = range(9)
 
 
 @dataclass(frozen=True)
@@ -44,7 +44,7 @@ class Workload:
     steps: int
     warmup: int          # FP32 steps before the state is quantized
     rounding: int
-    bits_policy: str     # "int8" | "alpha_gt_0.99" | "rank_half"
+    bits_policy: str     # "int8" | "alpha_gt_0.99" | "rank_half" | "channel_half"
     layers: int = 1
     axis: int = 0        # scale groups: 0 value axis (G key columns), 1 key axis (G value rows)
 
@@ -73,6 +73,11 @@ WORKLOADS = {
     # KDA (per-key-channel decay with delta correction) at the GLA shape: alpha_j as GLA's,
     # beta as Gated DeltaNet's; INT8, group 64, SR.
     5: Workload(5, "kda_b256_h16_d128_int8_g64_sr", KDA, 256, 16, 128, 128, 64, 512, 32, SR, "int8"),
+    # GLA with a persistent decay rate per key channel: alpha_j = sigmoid(mu_hj + N(0, 0.5^2))
+    # ^(1/16), mu_hj ~ N(3, 1) sorted descending inside each head (channels ordered by decay);
+    # per head the slower half of the 32-channel groups INT8, the rest INT4; SR.
+    6: Workload(6, "gla_b256_h16_d128_chmix_g32_sr", GLA, 256, 16, 128, 128, 32, 512, 32, SR,
+                "channel_half"),
 }
 
 
@@ -105,6 +110,25 @@ def head_retention(w: Workload, seed: int = 0, layer: int = 0) -> np.ndarray:
     return np.ones(w.H, np.float32)
 
 
+def channel_mu(w: Workload, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """Persistent per-(head, key channel) decay logit mu_hj ~ N(3, 1), sorted
+    descending inside each head ("channel_half" policy)."""
+    mu = _rng(seed, w.wid, _CHAN_MU, layer).standard_normal((w.H, w.dk)) + 3.0
+    return -np.sort(-mu, axis=1)
+
+
+def channel_retention(w: Workload, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """Per-(head, key channel) decay statistic sigmoid(mu_hj)^(1/16), float32 [H][dk]."""
+    mu = channel_mu(w, seed, layer)
+    return ((1.0 / (1.0 + np.exp(-mu))) ** (1.0 / 16.0)).astype(np.float32)
+
+
+def group_retention(w: Workload, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """Mean channel retention of each value-axis group of G key channels, [H][dk/G]."""
+    r = channel_retention(w, seed, layer).astype(np.float64)
+    return r.reshape(w.H, w.dk // w.G, w.G).mean(axis=2).astype(np.float32)
+
+
 def head_alpha(w: Workload, seed: int = 0) -> np.ndarray:
     """Per-head constant alpha_h ~ U(0.90, 0.999) (alpha_gt_0.99 policy)."""
     return _rng(seed, w.wid, _HEAD_ALPHA).uniform(0.90, 0.999, w.H).astype(np.float32)
@@ -125,7 +149,11 @@ def step_inputs(w: Workload, t: int, seed: int = 0, layer: int = 0):
     k = _unit(_normal(_rng(seed, w.wid, _K, t, layer), (B, H, dk)))
     v = _normal(_rng(seed, w.wid, _V, t, layer), (B, H, dv))
     if w.mixer in (GLA, KDA):
-        z = _normal(_rng(seed, w.wid, _ALPHA, t, layer), (B, H, dk)).astype(np.float64) + 3.0
+        z = _normal(_rng(seed, w.wid, _ALPHA, t, layer), (B, H, dk)).astype(np.float64)
+        if w.bits_policy == "channel_half":
+            z = channel_mu(w, seed, layer)[None] + 0.5 * z
+        else:
+            z = z + 3.0
         alpha = ((1.0 / (1.0 + np.exp(-z))) ** (1.0 / 16.0)).astype(np.float32)
         if w.mixer == GLA:
             return q, k, v, alpha, None
