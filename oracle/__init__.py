@@ -41,7 +41,8 @@ class Cfg(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("G", ctypes.c_int32), ("mixer", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("layer", ctypes.c_uint32), ("axis", ctypes.c_int32)]
+                ("layer", ctypes.c_uint32), ("axis", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 _lib = None
@@ -82,6 +83,13 @@ def lib():
             "oracle_readout": (None, [cp, _P, _P, _P, _P, _P]),
             "oracle_bits_by_decay": (i32, [_P, i32, i32, f32, ctypes.c_uint8,
                                            ctypes.c_uint8, _P]),
+            "oracle_fp8_decode": (f32, [ctypes.c_uint8]),
+            "oracle_fp8_encode": (ctypes.c_uint8, [f32]),
+            "oracle_window_bytes": (ctypes.c_size_t, [cp]),
+            "oracle_head_step_pw": (None, [cp, i32, i32, _P, _P, _P, _P, _P, _P, _P, _P, f32,
+                                           _P, u64, _P, _P]),
+            "oracle_head_window_state": (None, [cp, _P, _P, _P, _P, u64, _P]),
+            "oracle_head_window_readout": (None, [cp, _P, _P, _P, _P, u64, _P, _P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -100,8 +108,9 @@ def _f32(a):
     return a
 
 
-def cfg(B, H, dk, dv, G, mixer=GDN, rounding=RTN, seed=0, layer=0, axis=VALUE_AXIS) -> Cfg:
-    return Cfg(B, H, dk, dv, G, mixer, rounding, seed, layer, axis)
+def cfg(B, H, dk, dv, G, mixer=GDN, rounding=RTN, seed=0, layer=0, axis=VALUE_AXIS,
+        window=0) -> Cfg:
+    return Cfg(B, H, dk, dv, G, mixer, rounding, seed, layer, axis, window)
 
 
 def scales_shape(c: Cfg):
@@ -327,3 +336,50 @@ def bits_by_decay(retention, mode, thr_or_frac, lo=4, hi=8):
     if rc != 0:
         raise ValueError("bits_by_decay: bad arguments")
     return out
+
+
+# ---- pure-write window ---------------------------------------------------------
+
+def fp8_decode(code: int) -> float:
+    return lib().oracle_fp8_decode(code)
+
+
+def fp8_encode(x: float) -> int:
+    return lib().oracle_fp8_encode(x)
+
+
+def window_bytes(c: Cfg) -> int:
+    return lib().oracle_window_bytes(ctypes.byref(c))
+
+
+def head_step_pw(c: Cfg, b, h, bits, codes, scales, window, q, k, v, alpha, beta, step,
+                 want_pre=False, want_xval=False):
+    """One quantized step of one head with its pure-write window (updated in place)."""
+    bb = block_bits(c, bits)
+    assert codes.size == head_code_bytes(c, bb) and window.size == window_bytes(c)
+    assert window.dtype == np.uint8 and window.flags.c_contiguous
+    q, k, v, alpha = _f32(q), _f32(k), _f32(v), _f32(alpha)
+    o = np.zeros(c.dv, np.float32)
+    pre = np.zeros((c.dv, c.dk), np.float32) if want_pre else None
+    xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
+    lib().oracle_head_step_pw(ctypes.byref(c), b, h, _ptr(bb), _ptr(codes), _ptr(scales),
+                              _ptr(window), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), float(beta),
+                              _ptr(o), step, _ptr(pre), _ptr(xval))
+    return o, pre, xval
+
+
+def head_window_state(c: Cfg, bits, codes, scales, window, step):
+    S = np.zeros((c.dv, c.dk), np.float32)
+    lib().oracle_head_window_state(ctypes.byref(c), _ptr(block_bits(c, bits)),
+                                   _ptr(np.ascontiguousarray(codes)), _ptr(_f32(scales)),
+                                   _ptr(np.ascontiguousarray(window)), step, _ptr(S))
+    return S
+
+
+def head_window_readout(c: Cfg, bits, codes, scales, window, step, q):
+    o = np.zeros(c.dv, np.float32)
+    lib().oracle_head_window_readout(ctypes.byref(c), _ptr(block_bits(c, bits)),
+                                     _ptr(np.ascontiguousarray(codes)), _ptr(_f32(scales)),
+                                     _ptr(np.ascontiguousarray(window)), step, _ptr(_f32(q)),
+                                     _ptr(o))
+    return o

@@ -434,6 +434,204 @@ void oracle_head_readout(const oracle_cfg* c, const uint8_t* block_bits, const u
 }
 
 // ---------------------------------------------------------------------------
+// Pure-write window ("Low-Bit GDN Recurrent-State Quantization: ... Pure-Write
+// Sliding Windows", abstract): the last W pure writes are kept apart from the
+// low-bit state as FP8 vector pairs (a, b), so that the full state is
+// H + sum a b^T; every step propagates each pair through the state
+// transition (b <- A^T b), and a pair is added into H only when it leaves
+// the window.  Readings (the abstract fixes no format or order): FP8 is OCP
+// E4M3 with one absmax scale per vector (s = max|x| / 448); the pair pushed
+// at counter t lives in slot t mod W, so slot t mod W holds the oldest pair
+// at counter t; an empty slot has zero scales and contributes exactly 0.
+//
+// Window area of one head: a codes [dv][W], b codes [W][dk], then the scales
+// [W][2] (s_a, s_b), padded to a multiple of 16 bytes.
+// ---------------------------------------------------------------------------
+
+// OCP E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0 holds
+// the subnormals m/8 * 2^-6; 0x7F and 0xFF are NaN; no infinities; 448 is
+// the largest finite value.
+float oracle_fp8_decode(uint8_t code) {
+  const int e = (code >> 3) & 0xF, m = code & 7;
+  const float sign = (code & 0x80) ? -1.0f : 1.0f;
+  if (e == 15 && m == 7) return std::nanf("");
+  if (e == 0) return sign * std::ldexp((float)m, -9);
+  return sign * std::ldexp(1.0f + (float)m / 8.0f, e - 7);
+}
+
+// Nearest E4M3 value to a finite x with |x| <= 448, ties to the even
+// mantissa; the sign is kept (also for results of zero).
+uint8_t oracle_fp8_encode(float x) {
+  const uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
+  const double a = std::fabs((double)x);
+  int best = 0;
+  double best_err = a;  // code 0 (+0)
+  for (int c = 1; c < 0x7F; ++c) {
+    const double err = std::fabs((double)oracle_fp8_decode((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+size_t oracle_window_bytes(const oracle_cfg* c) {
+  const size_t W = (size_t)c->window;
+  const size_t raw = (size_t)c->dv * W + W * (size_t)c->dk + 8 * W;
+  return (raw + 15) / 16 * 16;
+}
+
+namespace {
+
+struct Window {
+  const oracle_cfg* c;
+  uint8_t* base;
+  uint8_t* acode(int i, int t) const { return base + (size_t)i * c->window + t; }
+  uint8_t* bcode(int t, int j) const {
+    return base + (size_t)c->dv * c->window + (size_t)t * c->dk + j;
+  }
+  float* scale(int t, int which) const {
+    return reinterpret_cast<float*>(base + (size_t)c->dv * c->window +
+                                    (size_t)c->window * c->dk) + 2 * t + which;
+  }
+};
+
+// Encode x[0..n) with one absmax scale: codes and the scale.
+void fp8_vector(const float* x, int n, uint8_t* codes, size_t stride, float* scale) {
+  float m = 0.0f;
+  for (int j = 0; j < n; ++j) m = std::max(m, std::fabs(x[j]));
+  float s, inv;
+  oracle_group_scale(m, 448, &s, &inv);
+  *scale = s;
+  for (int j = 0; j < n; ++j) codes[(size_t)j * stride] = oracle_fp8_encode(x[j] * inv);
+}
+
+// Slot order by age at counter t: oldest first.
+int age_slot(const oracle_cfg* c, uint64_t t, int age) {
+  return (int)((t + (uint64_t)age) % (uint64_t)c->window);
+}
+
+}  // namespace
+
+void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
+                         uint8_t* codes, float* scales, uint8_t* window,
+                         const float* q, const float* k, const float* v,
+                         const float* alpha, float beta, float* o, uint64_t step,
+                         float* pre, double* xval) {
+  const int dk = c->dk, dv = c->dv, W = c->window;
+  const Layout L = head_layout(c, block_bits);
+  const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
+  const Window win{c, window};
+  const int slot = (int)(step % (uint64_t)W);
+  const bool delta = delta_rule(c->mixer);
+  auto decay = [&](int j) { return vector_decay(c->mixer) ? alpha[j] : alpha[0]; };
+
+  // propagated keys b' = A^T b of every pair, and c_t = b'.q
+  std::vector<float> Bp((size_t)W * dk), A((size_t)W * dv), cq(W), db(dk);
+  for (int t = 0; t < W; ++t) {
+    const float sa = *win.scale(t, 0), sb = *win.scale(t, 1);
+    for (int i = 0; i < dv; ++i) A[(size_t)t * dv + i] = oracle_fp8_decode(*win.acode(i, t)) * sa;
+    for (int j = 0; j < dk; ++j) db[j] = (oracle_fp8_decode(*win.bcode(t, j)) * sb) * decay(j);
+    float* bp = Bp.data() + (size_t)t * dk;
+    if (delta) {
+      const float wb = -(beta * oracle_dot(db.data(), k, dk));
+      for (int j = 0; j < dk; ++j) bp[j] = std::fma(wb, k[j], db[j]);
+    } else {
+      for (int j = 0; j < dk; ++j) bp[j] = db[j];
+    }
+    cq[t] = oracle_dot(bp, q, dk);
+  }
+  // the new pure write (a, b) = (weight * v, k)
+  std::vector<float> anew(dv);
+  for (int i = 0; i < dv; ++i) anew[i] = (c->mixer == kMixerGLA) ? v[i] : beta * v[i];
+  const float cnew = oracle_dot(k, q, dk);
+
+  // H' = H A + a_o b_o^T (the pair in `slot` leaves), o = H'q + window terms
+  std::vector<float> d(dk), Sp((size_t)dv * dk), stored((size_t)dv * dk);
+  const float* bo = Bp.data() + (size_t)slot * dk;
+  for (int i = 0; i < dv; ++i) {
+    float* sp = Sp.data() + (size_t)i * dk;
+    for (int j = 0; j < dk; ++j) {
+      const float code = (float)get_code_at(L, codes, i, j);
+      const float s = scales[scale_index(c, i, j)];
+      stored[(size_t)i * dk + j] = code * s;
+      d[j] = vector_decay(c->mixer) ? (code * s) * alpha[j] : code * (s * alpha[0]);
+    }
+    const float ao = A[(size_t)slot * dv + i];
+    if (delta) {
+      const float wh = -(beta * oracle_dot(d.data(), k, dk));
+      for (int j = 0; j < dk; ++j) sp[j] = std::fma(ao, bo[j], std::fma(wh, k[j], d[j]));
+    } else {
+      for (int j = 0; j < dk; ++j) sp[j] = std::fma(ao, bo[j], d[j]);
+    }
+    if (o) {
+      float acc = oracle_dot(sp, q, dk);
+      for (int age = 1; age < W; ++age) {
+        const int t = age_slot(c, step, age);
+        acc = std::fma(A[(size_t)t * dv + i], cq[t], acc);
+      }
+      o[i] = std::fma(anew[i], cnew, acc);
+    }
+  }
+  if (pre) std::memcpy(pre, Sp.data(), sizeof(float) * Sp.size());
+  quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, xval);
+
+  // store the window: propagated keys of the remaining pairs, the new pair
+  for (int t = 0; t < W; ++t) {
+    if (t == slot) continue;
+    fp8_vector(Bp.data() + (size_t)t * dk, dk, win.bcode(t, 0), 1, win.scale(t, 1));
+  }
+  fp8_vector(anew.data(), dv, win.acode(0, slot), (size_t)W, win.scale(slot, 0));
+  fp8_vector(k, dk, win.bcode(slot, 0), 1, win.scale(slot, 1));
+}
+
+// The full state H + sum a b^T (pairs oldest first) as the next step at
+// counter `step` would see it.
+void oracle_head_window_state(const oracle_cfg* c, const uint8_t* block_bits,
+                              const uint8_t* codes, const float* scales,
+                              const uint8_t* window, uint64_t step, float* S) {
+  const int dk = c->dk, dv = c->dv, W = c->window;
+  oracle_head_dequantize(c, block_bits, codes, scales, S);
+  const Window win{c, const_cast<uint8_t*>(window)};
+  for (int age = 0; age < W; ++age) {
+    const int t = age_slot(c, step, age);
+    const float sa = *win.scale(t, 0), sb = *win.scale(t, 1);
+    for (int i = 0; i < dv; ++i) {
+      const float a = oracle_fp8_decode(*win.acode(i, t)) * sa;
+      for (int j = 0; j < dk; ++j)
+        S[(size_t)i * dk + j] =
+            std::fma(a, oracle_fp8_decode(*win.bcode(t, j)) * sb, S[(size_t)i * dk + j]);
+    }
+  }
+}
+
+// Readout of the stored full state: o = H q + sum a (b.q), pairs oldest first.
+void oracle_head_window_readout(const oracle_cfg* c, const uint8_t* block_bits,
+                                const uint8_t* codes, const float* scales,
+                                const uint8_t* window, uint64_t step, const float* q,
+                                float* o) {
+  const int dk = c->dk, dv = c->dv, W = c->window;
+  std::vector<float> H((size_t)dv * dk), bb(dk);
+  oracle_head_dequantize(c, block_bits, codes, scales, H.data());
+  const Window win{c, const_cast<uint8_t*>(window)};
+  std::vector<float> cq(W);
+  for (int t = 0; t < W; ++t) {
+    const float sb = *win.scale(t, 1);
+    for (int j = 0; j < dk; ++j) bb[j] = oracle_fp8_decode(*win.bcode(t, j)) * sb;
+    cq[t] = oracle_dot(bb.data(), q, dk);
+  }
+  for (int i = 0; i < dv; ++i) {
+    float acc = oracle_dot(H.data() + (size_t)i * dk, q, dk);
+    for (int age = 0; age < W; ++age) {
+      const int t = age_slot(c, step, age);
+      acc = std::fma(oracle_fp8_decode(*win.acode(i, t)) * *win.scale(t, 0), cq[t], acc);
+    }
+    o[i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Whole batch, in the library's array layout.
 // ---------------------------------------------------------------------------
 

@@ -40,6 +40,7 @@ typedef struct {
   int32_t axis;     /* 0 value-axis groups (G key columns of one row, scales
                        [dv][dk/G]); 1 key-axis groups (G value rows of one
                        column, scales [dv/G][dk])                       */
+  int32_t window;   /* pure-write window length W (0: none)             */
 } oracle_cfg;
 
 /* ---- counter-based random bits ---- */
@@ -106,6 +107,23 @@ void oracle_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
 void oracle_readout(const oracle_cfg* c, const uint8_t* block_bits,
                     const uint8_t* codes, const float* scales, const float* q,
                     float* o);
+
+/* ---- pure-write window: W FP8 (E4M3) pairs per head, see oracle.cpp ---- */
+float oracle_fp8_decode(uint8_t code);
+uint8_t oracle_fp8_encode(float x);
+size_t oracle_window_bytes(const oracle_cfg* c);
+void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
+                         uint8_t* codes, float* scales, uint8_t* window,
+                         const float* q, const float* k, const float* v,
+                         const float* alpha, float beta, float* o, uint64_t step,
+                         float* pre, double* xval);
+void oracle_head_window_state(const oracle_cfg* c, const uint8_t* block_bits,
+                              const uint8_t* codes, const float* scales,
+                              const uint8_t* window, uint64_t step, float* S);
+void oracle_head_window_readout(const oracle_cfg* c, const uint8_t* block_bits,
+                                const uint8_t* codes, const float* scales,
+                                const uint8_t* window, uint64_t step, const float* q,
+                                float* o);
 
 /* ---- decay-based bit allocation (LoReS 2/4) ---- */
 int oracle_bits_by_decay(const float* retention, int heads, int mode,
