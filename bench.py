@@ -53,7 +53,8 @@ def kernel_source_hash() -> str:
 
 
 def traffic_key(w) -> str:
-    return f"{w.name}|{ROUNDING_NAMES[w.rounding]}|{'key' if w.axis else 'value'}-axis"
+    key = f"{w.name}|{ROUNDING_NAMES[w.rounding]}|{'key' if w.axis else 'value'}-axis"
+    return key + (f"|window{w.window}" if w.window else "")
 
 
 def measured_traffic(w):
@@ -102,6 +103,9 @@ def algorithmic_bytes(w, bb) -> int:
     per_b = 0
     for h in range(w.H):
         state = w.dv * int(np.sum(2 * bb[h].astype(np.int64))) + w.dv * w.dk // w.G * 4
+        if w.window:  # pure-write window: a codes read + the new pair's, keys and scales
+            W = w.window
+            per_b += w.dv * W + w.dv + 2 * (W * w.dk + 8 * W)
         io = 4 * (2 * w.dk + 2 * w.dv)
         per_b += 2 * state + io + gate_bytes(w)
     return per_b * w.B
@@ -118,7 +122,7 @@ def cpu_baseline(w, hb, seconds: float):
     import workloads as W
 
     rng = np.random.default_rng(0)
-    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0, w.axis)
+    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0, w.axis, w.window)
     q, k, v, alpha, beta = W.step_inputs(w, 0)
     heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096), rng.integers(0, w.H, 4096))]
     S0 = rng.standard_normal((w.dv, w.dk)).astype(np.float32)
@@ -128,11 +132,17 @@ def cpu_baseline(w, hb, seconds: float):
     while time.perf_counter() - t0 < seconds:
         b, h = heads[n % len(heads)]
         if (b, h) not in states:
-            states[(b, h)] = oracle.head_quantize(c, b, h, hb[h], S0, 0)[:2]
-        codes, scales = states[(b, h)]
+            states[(b, h)] = oracle.head_quantize(c, b, h, hb[h], S0, 0)[:2] + (
+                np.zeros(oracle.window_bytes(c), np.uint8),)
+        codes, scales, win = states[(b, h)]
         a = alpha[b, h] if w.mixer in (W.GLA, W.KDA) else np.float32([alpha[b, h]])
-        oracle.head_step(c, b, h, hb[h], codes, scales, q[b, h], k[b, h], v[b, h], a,
-                         0.0 if beta is None else float(beta[b, h]), 1 + n)
+        bt = 0.0 if beta is None else float(beta[b, h])
+        if w.window:
+            oracle.head_step_pw(c, b, h, hb[h], codes, scales, win, q[b, h], k[b, h], v[b, h], a,
+                                bt, 1 + n)
+        else:
+            oracle.head_step(c, b, h, hb[h], codes, scales, q[b, h], k[b, h], v[b, h], a, bt,
+                             1 + n)
         n += 1
     dt = time.perf_counter() - t0
     heads_per_s = n / dt
@@ -156,6 +166,8 @@ def main():
     ap.add_argument("--rounding", type=int, default=None, help="override: 0 RTN, 1 SR, 2 BDR")
     ap.add_argument("--axis", type=int, default=0,
                     help="scale groups: 0 value axis (default), 1 key axis")
+    ap.add_argument("--window", type=int, default=0,
+                    help="pure-write window length (0 = none, 4, 8, 16)")
     ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
     ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -179,7 +191,7 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.rounding is not None:
         w = w.scaled(rounding=args.rounding)
-    w = w.scaled(axis=args.axis)
+    w = w.scaled(axis=args.axis, window=args.window)
     hb = block_bits(w, Q)  # [H][dk/16]
     uniform = bool(np.all(hb == hb[:, :1]))
     nbytes = algorithmic_bytes(w, hb)
@@ -187,7 +199,7 @@ def main():
     def qcfg(layer):
         return Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False,
                         hb[:, 0].tolist() if uniform else None, 0, layer, w.axis,
-                        None if uniform else hb.tolist())
+                        None if uniform else hb.tolist(), w.window)
 
     cfg0 = qcfg(0)
     cb, sb = Q.qstate_state_bytes(cfg0)
@@ -252,7 +264,8 @@ def main():
                            {f"{b}-bit 16-channel blocks": int((hb == b).sum())
                             for b in sorted(set(hb.ravel().tolist()))}),
             "rounding": ROUNDING_NAMES[w.rounding],
-            "group_axis": "key" if w.axis else "value", "state_instances": n_states,
+            "group_axis": "key" if w.axis else "value", "window": w.window,
+            "state_instances": n_states,
             "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,
         },
         "hbm_gbps": gbps,

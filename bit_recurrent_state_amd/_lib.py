@@ -36,7 +36,7 @@ class QStateConfig(ctypes.Structure):
         ("rounding", ctypes.c_int32), ("fp32_state", ctypes.c_int32),
         ("head_bits", ctypes.POINTER(ctypes.c_uint8)), ("seed", ctypes.c_uint64),
         ("layer", ctypes.c_uint32), ("group_axis", ctypes.c_int32),
-        ("channel_bits", ctypes.POINTER(ctypes.c_uint8)),
+        ("channel_bits", ctypes.POINTER(ctypes.c_uint8)), ("window", ctypes.c_int32),
     ]
 
 

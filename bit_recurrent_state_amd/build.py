@@ -17,12 +17,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqstate.so")
-SOURCES = ([os.path.join(CSRC, f"qstate_{axis}_dk{dk}.hip")
-            for axis in ("value", "key") for dk in (64, 128, 256)]
+SOURCES = ([os.path.join(CSRC, f"qstate_window_dk{dk}_w{w}.hip")
+            for dk in (64, 128, 256) for w in (4, 8, 16)]
+           + [os.path.join(CSRC, f"qstate_{kind}_dk{dk}.hip")
+              for kind in ("value", "key") for dk in (64, 128, 256)]
            + [os.path.join(CSRC, "qstate_dispatch.cpp"), os.path.join(CSRC, "qstate_api.cpp")])
 HEADERS = [os.path.join(ROOT, "include", "qstate.h")] + [
     os.path.join(CSRC, h) for h in ("qstate_launch.h", "qstate_device.h", "qstate_value.h",
-                                    "qstate_key.h")]
+                                    "qstate_key.h", "qstate_window.h")]
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -77,6 +77,12 @@ int check_config(const qstate_config* c) {
         }
     }
   }
+  if (!c->fp32_state && c->window != 0) {
+    if (c->window < 0) return QSTATE_E_INVALID;
+    // the window kernels take value-axis groups and heads of one width
+    if (c->window != 4 && c->window != 8 && c->window != 16) return QSTATE_E_UNSUPPORTED;
+    if (c->group_axis != QSTATE_VALUE_AXIS || c->channel_bits) return QSTATE_E_UNSUPPORTED;
+  }
   if (c->dk != 64 && c->dk != 128 && c->dk != 256) return QSTATE_E_UNSUPPORTED;
   if (c->heads > kMaxHeads || c->dv > kMaxDv) return QSTATE_E_UNSUPPORTED;
   if (!c->fp32_state && c->group != 16 && c->group != 32 && c->group != 64 && c->group != 128)
@@ -86,6 +92,15 @@ int check_config(const qstate_config* c) {
   if (elems * 4.0 > 9.0e18 || (double)c->batch * c->heads * ((c->dv + 31) / 32) > 2147483647.0)
     return QSTATE_E_UNSUPPORTED;
   return QSTATE_OK;
+}
+
+uint64_t align16(uint64_t n) { return (n + 15) / 16 * 16; }
+
+// Bytes of one head's pure-write window area: a codes [dv][W], then two
+// copies of (b codes [W][dk], scales [W][2]).
+uint64_t window_head_bytes(const qstate_config* c) {
+  const uint64_t W = c->fp32_state ? 0 : (uint64_t)c->window;
+  return W ? align16((uint64_t)c->dv * W + 2 * (W * c->dk + 8 * W)) : 0;
 }
 
 void layout(const qstate_config* c, size_t* codes_bytes, size_t* scales_bytes, uint64_t* per_b) {
@@ -100,6 +115,8 @@ void layout(const qstate_config* c, size_t* codes_bytes, size_t* scales_bytes, u
   for (int h = 0; h < c->heads; ++h)
     for (int q = 0; q < c->dk / 16; ++q) pb += (uint64_t)c->dv * 2 * block_width(c, h, q);
   *codes_bytes = (size_t)pb * c->batch;
+  if (c->window)  // the window areas follow the codes
+    *codes_bytes = (size_t)(align16(*codes_bytes) + bh * window_head_bytes(c));
   const size_t per_head = c->group_axis == QSTATE_KEY_AXIS
                               ? (size_t)(c->dv / c->group) * c->dk
                               : (size_t)c->dv * (c->dk / c->group);
@@ -141,6 +158,11 @@ qs::KParams base_params(const qstate* s) {
   p.seed = s->cfg.seed;
   p.layer = s->cfg.layer;
   p.step = s->step;
+  if (!s->cfg.fp32_state && s->cfg.window > 0) {
+    p.window_len = s->cfg.window;
+    p.window_head_bytes = window_head_bytes(&s->cfg);
+    p.window = static_cast<uint8_t*>(s->state) + align16(s->bytes_per_b * s->cfg.batch);
+  }
   return p;
 }
 

@@ -127,6 +127,7 @@ __device__ __forceinline__ float lanes_max(float m) {
   if constexpr (LANES >= 2) m = fmaxf(m, dpp<kDppXor1>(m));
   if constexpr (LANES >= 4) m = fmaxf(m, dpp<kDppXor2>(m));
   if constexpr (LANES >= 8) m = fmaxf(m, dpp<kDppHalfMirror>(m));
+  if constexpr (LANES >= 16) m = fmaxf(m, dpp<kDppMirror>(m));
   return m;
 }
 

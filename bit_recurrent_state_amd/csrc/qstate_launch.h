@@ -31,6 +31,9 @@ struct KParams {
   uint64_t seed;
   uint32_t layer;
   uint64_t step;         // stochastic-rounding counter of this event
+  uint8_t* window;       // pure-write window areas of all heads, or null
+  int32_t window_len;    // W: 0 (none), 4, 8 or 16
+  uint64_t window_head_bytes;  // bytes of one head's window area
 };
 
 enum Op { kStep = 0, kImport = 1, kExport = 2, kReadout = 3 };
@@ -41,14 +44,33 @@ enum Op { kStep = 0, kImport = 1, kExport = 2, kReadout = 3 };
 hipError_t launch(Op op, int mixer, int rounding, int fp32, int dk,
                   const KParams& p, hipStream_t stream);
 
-// Per-dk entry points of the kernel sources (qstate_value_dk*.hip,
-// qstate_key_dk*.hip), one translation unit each.
+// Per-dk (and per window length) entry points of the kernel sources
+// (qstate_value_dk*.hip, qstate_key_dk*.hip, qstate_window_dk*_w*.hip), one
+// translation unit each.
 hipError_t launch_value_dk64(Op op, int mixer, int rounding, int fp32, const KParams& p,
                              hipStream_t stream);
 hipError_t launch_value_dk128(Op op, int mixer, int rounding, int fp32, const KParams& p,
                               hipStream_t stream);
 hipError_t launch_value_dk256(Op op, int mixer, int rounding, int fp32, const KParams& p,
                               hipStream_t stream);
+hipError_t launch_window_dk64_w4(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk64_w8(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk64_w16(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk128_w4(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk128_w8(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk128_w16(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk256_w4(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk256_w8(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
+hipError_t launch_window_dk256_w16(Op op, int mixer, int rounding, const KParams& p,
+                                hipStream_t stream);
 hipError_t launch_key_dk64(Op op, int mixer, int rounding, const KParams& p, hipStream_t stream);
 hipError_t launch_key_dk128(Op op, int mixer, int rounding, const KParams& p, hipStream_t stream);
 hipError_t launch_key_dk256(Op op, int mixer, int rounding, const KParams& p, hipStream_t stream);

@@ -1,0 +1,13 @@
+// qstate_window_dk64_w4.hip — decode step with a pure-write window of W = 4
+// pairs for dk = 64.
+
+#include "qstate_window.h"
+
+namespace qs {
+
+hipError_t launch_window_dk64_w4(Op op, int mixer, int rounding, const KParams& p,
+                              hipStream_t stream) {
+  return launch_pw_g<64, 4>(op, mixer, rounding, p, stream);
+}
+
+}  // namespace qs

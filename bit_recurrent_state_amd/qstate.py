@@ -40,6 +40,7 @@ class Config:
     layer: int = 0
     group_axis: int = VALUE_AXIS
     channel_bits: Optional[Sequence[Sequence[int]]] = None  # [heads][dk/16], overrides head_bits
+    window: int = 0  # pure-write window length W (0, 4, 8 or 16)
 
     def to_c(self):
         """(QStateConfig, keep-alive buffers)."""
@@ -58,7 +59,7 @@ class Config:
             keep.append(cb)
         c = QStateConfig(self.batch, self.heads, self.dk, self.dv, self.group, self.mixer,
                          self.rounding, int(bool(self.fp32_state)), ptr, self.seed, self.layer,
-                         self.group_axis, cptr)
+                         self.group_axis, cptr, self.window)
         return c, keep
 
     def bits(self) -> np.ndarray:

@@ -91,6 +91,31 @@
  *                   (key axis)
  *   FP32 state      float [B][H][dv][dk]  (fp32_state = 1)
  *
+ * Pure-write window (cfg.window = W > 0; "Low-Bit GDN Recurrent-State
+ * Quantization ... Pure-Write Sliding Windows", abstract): the full state of
+ * a head is H + sum_t a_t b_t^T, H the low-bit state above and (a_t, b_t) the
+ * last W pure writes stored as OCP E4M3 vectors with one absmax scale each
+ * (s = max|x| / 448, inv = the largest float with inv * max|x| <= 448, code =
+ * E4M3 nearest-even of x * inv, value = decode(code) * s).  At counter t the
+ * pair in slot t mod W is the oldest; a step at counter t:
+ *   1. keys: b'_s = A^T b_s for every slot s: d_j = b_sj * alpha (or
+ *      alpha_j); with the delta rule b'_sj = fma(-(beta * dot(d, k)), k_j,
+ *      d_j), else b'_sj = d_j;  c_s = dot(b'_s, q);
+ *   2. H'_ij = fma(a_o,i, b'_o,j, fma(-(beta * u_i), k_j, d_ij)) with the
+ *      leaving pair o = t mod W (without the delta rule: fma(a_o,i, b'_o,j,
+ *      d_ij)); d, u as in steps 1-2 above;
+ *   3. new pair in slot o: a = w v (w = beta, or 1 for GLA), b = k;
+ *   4. o_i = dot(H'_i, q), then fma(a_s,i, c_s, .) over the other slots
+ *      oldest first, then fma(a_new,i, dot(k, q), .);
+ *   5. H' requantized as above; the kept pairs' b' and the new pair
+ *      re-encoded.
+ * Window area per head (after the codes, 16-byte aligned, heads in (b, h)
+ * order, each align16(dv*W + 2*(W*dk + 8*W)) bytes): a codes [dv][W], then two
+ * copies of (b codes [W][dk], scales [W][2] = (s_a, s_b)); counter t reads
+ * copy t & 1 and writes copy (t + 1) & 1.  An import empties the window
+ * (zero codes and scales, which contribute exactly nothing); export and
+ * readout return the full state.
+ *
  * Range: state magnitudes stay below 2^120 (far beyond any FP32 recurrence
  * that does not overflow within a few steps).
  *
@@ -164,6 +189,11 @@ typedef struct {
                                slowest-decaying channels; order channels so
                                that slow ones share blocks).  Value-axis
                                groups may not mix widths.  Copied at create. */
+  int32_t window;           /* W = 0 (none), 4, 8 or 16: keep the last W pure
+                               writes of each head as FP8 pairs beside its
+                               low-bit state (value-axis groups, heads of one
+                               width); their area follows the codes in the
+                               codes buffer (see the pure-write window below) */
 } qstate_config;
 
 typedef struct qstate qstate; /* opaque; host-side metadata only */

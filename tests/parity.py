@@ -118,9 +118,9 @@ class Run:
         uniform = bool(np.all(self.bb == self.bb[:, :1]))
         self.cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, False,
                             [int(x) for x in self.bb[:, 0]] if uniform else None, seed, layer,
-                            w.axis, None if uniform else self.bb.tolist())
+                            w.axis, None if uniform else self.bb.tolist(), w.window)
         self.ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, seed, layer,
-                               w.axis)
+                               w.axis, w.window)
         all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
         self.heads = all_heads if heads is None else list(heads)
         self.rep = Report()
@@ -135,6 +135,25 @@ class Run:
         off = oracle.head_offset(self.ocfg, b, h, self.bb)
         n = oracle.head_code_bytes(self.ocfg, self.bb[h])
         return off, n
+
+    # ---- pure-write window: the library's area (two key-side copies) -------------
+    def _win_lib(self, codes_np, b, h, counter):
+        """(a codes, b codes, scales) of head (b, h) in the library's window area as
+        the step at `counter` reads it."""
+        w = self.w
+        W = w.window
+        base = (oracle.codes_bytes(self.ocfg, self.bb) + 15) // 16 * 16
+        whb = (w.dv * W + 2 * (W * w.dk + 8 * W) + 15) // 16 * 16
+        area = codes_np[base + (b * w.H + h) * whb: base + (b * w.H + h + 1) * whb]
+        cp = w.dv * W + (counter & 1) * (W * w.dk + 8 * W)
+        return (area[:w.dv * W], area[cp:cp + W * w.dk],
+                area[cp + W * w.dk:cp + W * w.dk + 8 * W])
+
+    def _win_ref(self, win):
+        w = self.w
+        W = w.window
+        return (win[:w.dv * W], win[w.dv * W:w.dv * W + W * w.dk],
+                win[w.dv * W + W * w.dk:w.dv * W + W * w.dk + 8 * W])
 
     def _alpha_head(self, alpha, b, h):
         return alpha[b, h] if self.w.mixer in (W.GLA, W.KDA) else np.float32([alpha[b, h]])
@@ -173,12 +192,14 @@ class Run:
             return
         self.gpu = Q.QState(self.cfg)
         self.gpu.load_fp32(S_gpu)  # counter 0 -> 1
-        self.ref, xvals = {}, {}
+        self.ref, xvals, self.win = {}, {}, {}
         for (b, h) in self.heads:
             codes, scales, xv = oracle.head_quantize(self.ocfg, b, h, self.bb[h],
                                                      S_ref[(b, h)], 0, want_xval=True)
             self.ref[(b, h)] = (codes, scales)
             xvals[(b, h)] = xv
+            if w.window:
+                self.win[(b, h)] = np.zeros(oracle.window_bytes(self.ocfg), np.uint8)
         torch.cuda.synchronize()
         self.compare(step=0, o_gpu=None, o_ref=None, xvals=xvals)
 
@@ -193,9 +214,18 @@ class Run:
         o_ref, xvals = {}, {}
         for (b, h) in self.heads:
             codes, scales = self.ref[(b, h)]
-            o, _, xv = oracle.head_step(self.ocfg, b, h, self.bb[h], codes, scales, q[b, h],
-                                        k[b, h], v[b, h], self._alpha_head(alpha, b, h),
-                                        self._beta_head(beta, b, h), counter, want_xval=True)
+            if w.window:
+                o, _, xv = oracle.head_step_pw(self.ocfg, b, h, self.bb[h], codes, scales,
+                                               self.win[(b, h)], q[b, h], k[b, h], v[b, h],
+                                               self._alpha_head(alpha, b, h),
+                                               self._beta_head(beta, b, h), counter,
+                                               want_xval=True)
+            else:
+                o, _, xv = oracle.head_step(self.ocfg, b, h, self.bb[h], codes, scales,
+                                            q[b, h], k[b, h], v[b, h],
+                                            self._alpha_head(alpha, b, h),
+                                            self._beta_head(beta, b, h), counter,
+                                            want_xval=True)
             o_ref[(b, h)] = o
             xvals[(b, h)] = xv
         torch.cuda.synchronize()
@@ -220,6 +250,15 @@ class Run:
                                      f"first {bad[:4].ravel().tolist()}")
             if not np.array_equal(cg, cr):
                 self._exempt_or_fail(step, b, h, bits, cg, cr, xvals)
+            if w.window:  # the window is part of the stored state: bit-exact
+                counter = self.gpu.step_counter
+                for name, g, r in zip(("a codes", "b codes", "scales"),
+                                      self._win_lib(codes_g, b, h, counter),
+                                      self._win_ref(self.win[(b, h)])):
+                    if not np.array_equal(g, r):
+                        bad = np.nonzero(g != r)[0]
+                        raise AssertionError(f"step {step} head {(b, h)}: window {name} differ "
+                                             f"at {len(bad)} bytes, first {bad[:4].tolist()}")
             if o_gpu is not None:
                 ok, err = _close(o_gpu[b, h], o_ref[(b, h)])
                 self.rep.max_o_err = max(self.rep.max_o_err, err)
@@ -262,11 +301,18 @@ class Run:
         torch.cuda.synchronize()
         Sg = _to_np(S).reshape(w.B, w.H, w.dv, w.dk)
         og = _to_np(o).reshape(w.B, w.H, w.dv)
+        counter = self.gpu.step_counter
         for (b, h) in self.heads:
             codes, scales = self.ref[(b, h)]
-            Sr = oracle.head_dequantize(self.ocfg, self.bb[h], codes, scales)
+            if w.window:  # the full state: low-bit part plus the window's pairs
+                Sr = oracle.head_window_state(self.ocfg, self.bb[h], codes, scales,
+                                              self.win[(b, h)], counter)
+                orr = oracle.head_window_readout(self.ocfg, self.bb[h], codes, scales,
+                                                 self.win[(b, h)], counter, q[b, h])
+            else:
+                Sr = oracle.head_dequantize(self.ocfg, self.bb[h], codes, scales)
+                orr = oracle.head_readout(self.ocfg, self.bb[h], codes, scales, q[b, h])
             assert np.array_equal(Sg[b, h], Sr), f"export differs at head {(b, h)}"
-            orr = oracle.head_readout(self.ocfg, self.bb[h], codes, scales, q[b, h])
             ok, err = _close(og[b, h], orr)
             assert ok, f"readout differs at head {(b, h)}: {err}"
             self.rep.max_s_err = max(self.rep.max_s_err, float(np.abs(Sg[b, h] - Sr).max()))

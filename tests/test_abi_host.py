@@ -104,6 +104,22 @@ def test_channel_bits_rules(L):
     assert status([8, 6] + [8] * 22, group=16) == -1
 
 
+def test_window_rules_and_size(L):
+    """Window lengths 4, 8, 16 with value-axis groups and heads of one width;
+    its area follows the codes, 16-byte aligned."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    keep, hb = _bits(4, 8, 4)
+    c = _cfg(head_bits=hb, window=8)
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+    codes = 2 * 64 * 128 * (4 + 8 + 4) // 8
+    per_head = (64 * 8 + 2 * (8 * 128 + 8 * 8) + 15) // 16 * 16
+    assert cb.value == (codes + 15) // 16 * 16 + 2 * 3 * per_head
+    for kw, st in ((dict(window=5), -2), (dict(window=-1), -1), (dict(window=8, group_axis=1), -2),
+                   (dict(window=32), -2)):
+        c = _cfg(**kw)
+        assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == st, kw
+
+
 def test_bad_head_bits_and_pointers(L):
     keep, hb = _bits(4, 6, 8)
     c = _cfg(head_bits=hb)

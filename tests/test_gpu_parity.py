@@ -148,6 +148,46 @@ def test_channel_bits_full_size_sampled_heads():
     _run(w, 2, heads=sorted((i // w.H, i % w.H) for i in idx))
 
 
+WINDOW_RUNS = [(2, W.SR, 8), (3, W.RTN, 4), (5, W.BDR, 16), (4, W.SR, 8), (1, W.RTN, 16)]
+
+
+@pytest.mark.parametrize("wid,rounding,window", WINDOW_RUNS)
+def test_window_every_head(wid, rounding, window):
+    """Pure-write window: the low-bit state, the window's FP8 pairs and scales
+    bit-exact at every step, the readout and the exported full state."""
+    _run(W.WORKLOADS[wid].scaled(B=2, window=window), 2 * window + 3, rounding=rounding)
+
+
+def test_window_heads_split_over_waves():
+    """B=1: every head is split over several waves, which all read the window
+    while the first writes the next copy."""
+    w = W.WORKLOADS[0].scaled(window=8, dv=128, steps=20)
+    r = _run(w, 20)
+    assert r.steps == 20
+
+
+WINDOW_RAGGED = [
+    (W.GDN, W.SR, 64, 37, 16, [8, 4, 4], 8),
+    (W.KDA, W.RTN, 256, 45, 32, [4, 8], 4),
+    (W.GLA, W.BDR, 128, 70, 64, [8, 4], 16),
+    (W.SCALAR, W.SR, 256, 129, 128, [4], 8),
+]
+
+
+@pytest.mark.parametrize("mixer,rounding,dk,dv,G,bits,window", WINDOW_RAGGED)
+def test_window_shapes(mixer, rounding, dk, dv, G, bits, window):
+    w = W.Workload(65 + mixer, f"win_m{mixer}_dk{dk}_dv{dv}_g{G}_w{window}", mixer, 3, len(bits),
+                   dk, dv, G, 2 * window + 2, 3, rounding, "int8", window=window)
+    _run(w, 2 * window + 2, hb=np.array(bits, np.uint8), seed=17)
+
+
+def test_window_full_size_sampled_heads():
+    w = W.WORKLOADS[2].scaled(window=8)
+    rng = np.random.default_rng(41)
+    idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
+    _run(w, 10, heads=sorted((i // w.H, i % w.H) for i in idx))
+
+
 @pytest.mark.parametrize("layer", [0, 5])
 def test_config4_scalar_decay_layers(layer):
     _run(W.WORKLOADS[4].scaled(B=3), 8, layer=layer)

@@ -3,7 +3,7 @@ compute the documented semantics with fewer instructions.  Each identity is
 exact IEEE-754 binary32 arithmetic, so a C program with correctly rounded
 fmaf (no contraction) checks it exhaustively or on large random samples:
 
-1. s = m / r for r in {7, 127}: with c = RN(1/r), q = m*c, e = fma(-q, r, m),
+1. s = m / r for r in {7, 127, 448}: with c = RN(1/r), q = m*c, e = fma(-q, r, m),
    fma(e, c, q) == RN(m / r) for every float mantissa (three exponent ranges).
 2. Offset-binary dequantization: fma(c + 2^(b-1), sa, -2^(b-1)*sa) == RN(c*sa)
    for every code c and random (incl. subnormal) sa below 2^120, the library's
@@ -34,8 +34,8 @@ static float inv_rz(float m, float r){ float v = (float)((double)r / (double)m);
 int main(void){
   long bad = 0;
   /* 1 */
-  const float rs[2] = {7.0f, 127.0f};
-  for (int t = 0; t < 2; ++t) {
+  const float rs[3] = {7.0f, 127.0f, 448.0f};  /* INT4, INT8, FP8 (E4M3) vector scales */
+  for (int t = 0; t < 3; ++t) {
     const float r = rs[t], c = 1.0f / r;
     for (uint32_t mant = 0; mant < (1u << 23); ++mant)
       for (int ex = 0; ex < 3; ++ex) {

@@ -47,6 +47,7 @@ class Workload:
     bits_policy: str     # "int8" | "alpha_gt_0.99" | "rank_half" | "channel_half"
     layers: int = 1
     axis: int = 0        # scale groups: 0 value axis (G key columns), 1 key axis (G value rows)
+    window: int = 0      # pure-write window length W (0: none)
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
