@@ -154,6 +154,9 @@ qs::KParams base_params(const qstate* s) {
   p.slices = (units + units_per_slice - 1) / units_per_slice;
   p.bytes_per_b = s->bytes_per_b;
   std::memcpy(p.int8_blocks, s->int8_blocks, sizeof(p.int8_blocks));
+  const uint16_t full = (uint16_t)((1u << (s->cfg.dk / 16)) - 1u);
+  for (int h = 0; h < s->cfg.heads; ++h)
+    if (s->int8_blocks[h] != 0 && s->int8_blocks[h] != full) p.mixed = 1;
   std::memcpy(p.head_units, s->head_units, sizeof(p.head_units));
   p.seed = s->cfg.seed;
   p.layer = s->cfg.layer;

@@ -27,6 +27,7 @@ struct KParams {
                          // the key-axis block rows max(G, 4096/dk)
   uint64_t bytes_per_b;        // code bytes of one batch row (all heads)
   uint16_t int8_blocks[256];   // per head: bit q set = 16-column block q is INT8
+  int32_t mixed;               // some head mixes INT8 and INT4 blocks
   uint32_t head_units[256];    // per head: byte offset in a batch row / (8 dv)
   uint64_t seed;
   uint32_t layer;

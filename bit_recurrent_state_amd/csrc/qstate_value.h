@@ -500,16 +500,20 @@ __device__ __forceinline__ void aux_mixed_head(const KParams& p, const Slice sl)
 // Kernels and dispatch.
 // ---------------------------------------------------------------------------
 
-template <int MIXER, int RND, int DK, int G>
+// MIXED: the launch has heads of mixed widths; all its heads then take the
+// per-block path (one width per head otherwise, chosen per workgroup), so
+// that the kernels of one-width states carry no third path.
+template <int MIXER, int RND, int DK, int G, bool MIXED>
 __global__ __launch_bounds__(kThreads) void step_kernel(const KParams p) {
   const Slice sl = wave_slice(p);
-  const uint32_t m = p.int8_blocks[sl.h];
-  if (m == (1u << (DK / 16)) - 1u)
-    step_quant_head<MIXER, RND, DK, 8, G>(p, sl);
-  else if (m == 0u)
-    step_quant_head<MIXER, RND, DK, 4, G>(p, sl);
-  else
+  if constexpr (MIXED) {
     step_mixed_head<MIXER, RND, DK, G>(p, sl);
+  } else {
+    if (p.int8_blocks[sl.h] != 0u)
+      step_quant_head<MIXER, RND, DK, 8, G>(p, sl);
+    else
+      step_quant_head<MIXER, RND, DK, 4, G>(p, sl);
+  }
 }
 
 template <int MIXER, int DK>
@@ -517,16 +521,17 @@ __global__ __launch_bounds__(kThreads) void step_fp32_kernel(const KParams p) {
   step_fp32_head<MIXER, DK>(p, wave_slice(p));
 }
 
-template <int OP, bool SR, int DK, int G>
+template <int OP, bool SR, int DK, int G, bool MIXED>
 __global__ __launch_bounds__(kThreads) void aux_kernel(const KParams p) {
   const Slice sl = wave_slice(p);
-  const uint32_t m = p.int8_blocks[sl.h];
-  if (m == (1u << (DK / 16)) - 1u)
-    aux_quant_head<OP, SR, DK, 8, G>(p, sl);
-  else if (m == 0u)
-    aux_quant_head<OP, SR, DK, 4, G>(p, sl);
-  else
+  if constexpr (MIXED) {
     aux_mixed_head<OP, SR, DK, G>(p, sl);
+  } else {
+    if (p.int8_blocks[sl.h] != 0u)
+      aux_quant_head<OP, SR, DK, 8, G>(p, sl);
+    else
+      aux_quant_head<OP, SR, DK, 4, G>(p, sl);
+  }
 }
 
 template <int DK>
@@ -555,19 +560,19 @@ __global__ __launch_bounds__(kThreads) void readout_fp32_kernel(const KParams p)
 
 inline dim3 grid_of(const KParams& p) { return dim3((unsigned)(p.B * p.H * p.slices)); }
 
-template <int DK, int G>
+template <int DK, int G, bool MIXED>
 hipError_t launch_quant(Op op, int mixer, int rnd, const KParams& p, hipStream_t s) {
   const dim3 grid = grid_of(p), block(kThreads);
   if (op == kStep) {
-#define QS_STEP(M)                                                    \
-  if (mixer == M) {                                                   \
-    switch (rnd) {                                                    \
-      case kRTN: step_kernel<M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
-      case kSR: step_kernel<M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
-      case kBDR: step_kernel<M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
-      default: return hipErrorInvalidValue;                           \
-    }                                                                 \
-    return hipGetLastError();                                         \
+#define QS_STEP(M)                                                               \
+  if (mixer == M) {                                                              \
+    switch (rnd) {                                                               \
+      case kRTN: step_kernel<M, kRTN, DK, G, MIXED><<<grid, block, 0, s>>>(p); break; \
+      case kSR: step_kernel<M, kSR, DK, G, MIXED><<<grid, block, 0, s>>>(p); break;   \
+      case kBDR: step_kernel<M, kBDR, DK, G, MIXED><<<grid, block, 0, s>>>(p); break; \
+      default: return hipErrorInvalidValue;                                      \
+    }                                                                            \
+    return hipGetLastError();                                                    \
   }
     QS_STEP(kGDN) QS_STEP(kGLA) QS_STEP(kScalar) QS_STEP(kKDA)
 #undef QS_STEP
@@ -576,15 +581,15 @@ hipError_t launch_quant(Op op, int mixer, int rnd, const KParams& p, hipStream_t
   switch (op) {
     case kImport:  // nothing stored before an import: BDR rounds to nearest
       if (rnd == kSR)
-        aux_kernel<kImport, true, DK, G><<<grid, block, 0, s>>>(p);
+        aux_kernel<kImport, true, DK, G, MIXED><<<grid, block, 0, s>>>(p);
       else
-        aux_kernel<kImport, false, DK, G><<<grid, block, 0, s>>>(p);
+        aux_kernel<kImport, false, DK, G, MIXED><<<grid, block, 0, s>>>(p);
       return hipGetLastError();
     case kExport:
-      aux_kernel<kExport, false, DK, G><<<grid, block, 0, s>>>(p);
+      aux_kernel<kExport, false, DK, G, MIXED><<<grid, block, 0, s>>>(p);
       return hipGetLastError();
     case kReadout:
-      aux_kernel<kReadout, false, DK, G><<<grid, block, 0, s>>>(p);
+      aux_kernel<kReadout, false, DK, G, MIXED><<<grid, block, 0, s>>>(p);
       return hipGetLastError();
     default:
       return hipErrorInvalidValue;
@@ -614,10 +619,18 @@ hipError_t launch_value_dk(Op op, int mixer, int rnd, int fp32, const KParams& p
   }
   if (p.slice_rows % 32 != 0) return hipErrorInvalidValue;
   switch (p.G) {
-    case 16: return launch_quant<DK, 16>(op, mixer, rnd, p, s);
-    case 32: return launch_quant<DK, 32>(op, mixer, rnd, p, s);
-    case 64: return launch_quant<DK, 64>(op, mixer, rnd, p, s);
-    case 128: return launch_quant<DK, 128>(op, mixer, rnd, p, s);
+    case 16:
+      return p.mixed ? launch_quant<DK, 16, true>(op, mixer, rnd, p, s)
+                     : launch_quant<DK, 16, false>(op, mixer, rnd, p, s);
+    case 32:
+      return p.mixed ? launch_quant<DK, 32, true>(op, mixer, rnd, p, s)
+                     : launch_quant<DK, 32, false>(op, mixer, rnd, p, s);
+    case 64:
+      return p.mixed ? launch_quant<DK, 64, true>(op, mixer, rnd, p, s)
+                     : launch_quant<DK, 64, false>(op, mixer, rnd, p, s);
+    case 128:
+      return p.mixed ? launch_quant<DK, 128, true>(op, mixer, rnd, p, s)
+                     : launch_quant<DK, 128, false>(op, mixer, rnd, p, s);
     default: return hipErrorInvalidValue;
   }
 }
