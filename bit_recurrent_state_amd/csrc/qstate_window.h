@@ -95,14 +95,35 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// The W code bytes of a row (W / 4 words).
+template <int W>
+struct ARow {
+  uint32_t w[W / 4];
+};
+
+template <int W>
+__device__ __forceinline__ ARow<W> load_arow(const uint8_t* src) {
+  ARow<W> r;
+  if constexpr (W == 4) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(src);
+  } else if constexpr (W == 8) {
+    const uint2 t = *reinterpret_cast<const uint2*>(src);
+    r.w[0] = t.x, r.w[1] = t.y;
+  } else {
+    const uint4 t = *reinterpret_cast<const uint4*>(src);
+    r.w[0] = t.x, r.w[1] = t.y, r.w[2] = t.z, r.w[3] = t.w;
+  }
+  return r;
+}
+
 // The W code bytes of a row, rotated so that byte j belongs to the pair of
 // age j (slot `oldest` first).  W in {4, 8, 16}; `oldest` is wave-uniform.
 template <int W>
-__device__ __forceinline__ void age_order(const uint4 raw, int oldest, uint32_t (&r)[4]) {
+__device__ __forceinline__ void age_order(const ARow<W>& raw, int oldest, uint32_t (&r)[4]) {
   if constexpr (W == 4) {
-    r[0] = __builtin_amdgcn_alignbit(raw.x, raw.x, 8 * oldest);
+    r[0] = __builtin_amdgcn_alignbit(raw.w[0], raw.w[0], 8 * oldest);
   } else if constexpr (W == 8) {
-    uint32_t lo = raw.x, hi = raw.y;
+    uint32_t lo = raw.w[0], hi = raw.w[1];
     if (oldest >= 4) {
       const uint32_t t = lo;
       lo = hi, hi = t;
@@ -111,7 +132,7 @@ __device__ __forceinline__ void age_order(const uint4 raw, int oldest, uint32_t 
     r[0] = __builtin_amdgcn_alignbit(hi, lo, sh);
     r[1] = __builtin_amdgcn_alignbit(lo, hi, sh);
   } else {
-    uint32_t x[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t x[4] = {raw.w[0], raw.w[1], raw.w[2], raw.w[3]};
     const int dw = oldest >> 2;  // whole words first
     uint32_t y[4];
 #pragma unroll
@@ -228,52 +249,25 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
 
   const uint32_t key = SR ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
-  float kk[E], qq[E], al[E];
-  loadv(p.k + (size_t)sl.head * DK + col0, kk);
-  loadv(p.q + (size_t)sl.head * DK + col0, qq);
   float alpha_s = 0.0f, beta = 0.0f;
-  if constexpr (vector_decay(MIXER)) {
-    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
-  } else {
-#pragma unroll
-    for (int j = 0; j < E; ++j) al[j] = 0.0f;
-    alpha_s = p.alpha[sl.head];
-  }
+  if constexpr (!vector_decay(MIXER)) alpha_s = p.alpha[sl.head];
   if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
 
   // window of the head
   const WinHead wh = win_head(p, sl.head, DK, W);
   const int slot = (int)(p.step % (uint64_t)W);
-  float* lds_bo = lds;
-  float* lds_c = lds + DK;
-  float* lds_sa = lds_c + W;
-  float c_new, s_anew, inv_anew;
-  window_prologue<MIXER, DK, W>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
-                                lds_sa, c_new, s_anew, inv_anew);
-  __syncthreads();
-  float bo[E];
-  loadv(lds_bo + col0, bo);
-  float ca[W], sa[W];  // by age: 0 = oldest (leaving), W-1 = newest before this step
-#pragma unroll
-  for (int g = 0; g < W; ++g) {
-    const int t = (slot + g) % W;
-    ca[g] = uniform(lds_c[t]);
-    sa[g] = uniform(lds_sa[t]);
-  }
-  c_new = uniform(c_new);
-  inv_anew = uniform(inv_anew);
-  asm volatile("" ::: "memory");
-
+  // the state rows' loads go first, so that they are in flight while the
+  // per-head window work runs
   struct RowW {
     uint4 raw;
-    uint4 a;
+    ARow<W> a;
     float s0, s1, v;
   };
   auto load = [&](int it) {
     RowW in;
     const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
     in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
-    in.a = *reinterpret_cast<const uint4*>(wh.a + (size_t)row * W);
+    in.a = load_arow<W>(wh.a + (size_t)row * W);
     in.s0 = hscales[(size_t)row * ngr + gcol];
     in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
     in.v = vh[row];
@@ -285,6 +279,34 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
     ring[k] = load(k);
     asm volatile("" ::: "memory");
   }
+  float* lds_bo = lds;
+  float* lds_c = lds + DK;
+  float* lds_sa = lds_c + W;
+  float c_new, s_anew, inv_anew;
+  window_prologue<MIXER, DK, W>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
+                                lds_sa, c_new, s_anew, inv_anew);
+  __syncthreads();
+  float ca[W], sa[W];  // by age: 0 = oldest (leaving), W-1 = newest before this step
+#pragma unroll
+  for (int g = 0; g < W; ++g) {
+    const int t = (slot + g) % W;
+    ca[g] = uniform(lds_c[t]);
+    sa[g] = uniform(lds_sa[t]);
+  }
+  c_new = uniform(c_new);
+  inv_anew = uniform(inv_anew);
+  // per-head vectors in the rows' lane layout, after the window work
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  if constexpr (vector_decay(MIXER)) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+  }
+  asm volatile("" ::: "memory");
+
   const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
   for (int t = 0; t < n_trips; ++t) {
 #pragma unroll
@@ -310,8 +332,12 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
 #pragma unroll
         for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], j < 16 ? sa0 : sa1, j < 16 ? nb0 : nb1);
       }
-      // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A)
+      // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A); its key
+      // is read from LDS each iteration rather than held in E registers
       const float a_o = __builtin_amdgcn_cvt_f32_fp8((int)ab[0], 0) * sa[0];
+      float bo[E];
+      asm volatile("" ::: "memory");
+      loadv(lds_bo + col0, bo);
       if constexpr (delta_rule(MIXER)) {
         const float wt = -(beta * row_sum<LPR>(lane_dot(d, kk)));
 #pragma unroll
@@ -428,7 +454,7 @@ __device__ __forceinline__ void aux_pw_head(const KParams& p, const Slice sl, fl
         d[j] = __builtin_fmaf(d[j], s, -bias * s);
       }
       uint32_t ab[4] = {0u, 0u, 0u, 0u};
-      age_order<W>(*reinterpret_cast<const uint4*>(wh.a + (size_t)rr * W), oldest, ab);
+      age_order<W>(load_arow<W>(wh.a + (size_t)rr * W), oldest, ab);
       if constexpr (OP == kExport) {
 #pragma unroll
         for (int g = 0; g < W; ++g) {
