@@ -342,3 +342,68 @@ def test_zero_state_stays_zero():
         a.step(*map(_dev, (q, k, np.zeros_like(v), alpha, beta)), o)
         torch.cuda.synchronize()
         assert torch.all(a.codes == 0) and torch.all(a.scales == 0) and torch.all(o == 0)
+
+
+# ---- limits and extreme magnitudes -----------------------------------------------
+
+def test_most_heads_mixed_bits():
+    """256 heads (the most a state may have) with random widths: the per-head
+    offset table and INT8 masks up to the last head."""
+    rng = np.random.default_rng(51)
+    bits = rng.choice([4, 8], 256).astype(np.uint8)
+    w = W.Workload(60, "heads256", W.GDN, 2, 256, 64, 16, 16, 3, 2, W.SR, "int8")
+    _run(w, 3, hb=bits, seed=3)
+
+
+def test_most_rows():
+    """dv = 4096 rows (the most a head may have), every row checked."""
+    w = W.Workload(61, "rows4096", W.KDA, 1, 2, 128, 4096, 32, 2, 2, W.SR, "int8")
+    _run(w, 2, hb=np.array([4, 8], np.uint8), seed=5)
+
+
+@pytest.mark.parametrize("rounding", [W.RTN, W.SR, W.BDR])
+def test_extreme_magnitudes(rounding):
+    """Rows from about 1e-38 (subnormal scales, the tiny-group paths) up to
+    1e30, kept at their magnitude by pure decay steps (write weight 0):
+    codes and scales bit-exact, export exact."""
+    B, H, dk, dv, G = 1, 2, 128, 48, 32
+    hb = np.array([8, 4], np.uint8)
+    rng = np.random.default_rng(71)
+    mags = np.array([1e-38, 3e-37, 1e-30, 1e-20, 1e-10, 1.0, 1e10, 1e20, 1e30] * 6)[:dv]
+    S0 = (rng.standard_normal((B, H, dv, dk)) * mags[None, None, :, None]).astype(np.float32)
+    S0[0, 0, 3, :32] = 0.0  # an all-zero group
+    cfg = Q.Config(B, H, dk, dv, G, W.SCALAR, rounding, False, hb.tolist(), 9, 2)
+    st = Q.QState(cfg)
+    st.load_fp32(torch.from_numpy(S0.reshape(-1)).cuda())
+    oc = oracle.cfg(B, H, dk, dv, G, W.SCALAR, rounding, 9, 2)
+    ref = {}
+    for h in range(H):
+        ref[h] = oracle.head_quantize(oc, 0, h, int(hb[h]), S0[0, h], 0)[:2]
+    for t in range(1, 4):
+        q = rng.standard_normal((B, H, dk)).astype(np.float32)
+        k = rng.standard_normal((B, H, dk)).astype(np.float32)
+        v = rng.standard_normal((B, H, dv)).astype(np.float32)
+        alpha = np.float32(rng.uniform(0.5, 1.0, (B, H)))
+        dt = np.zeros((B, H), np.float32)  # write weight 0: S' = alpha S
+        log(f"[case] extreme magnitudes rounding={rounding} step={t}")
+        o = torch.empty(B * H * dv, device="cuda")
+        st.step(*map(_dev, (q, k, v, alpha, dt)), o)
+        torch.cuda.synchronize()
+        codes = st.codes.cpu().numpy()
+        scales = st.scales.cpu().numpy().reshape(B, H, -1)
+        for h in range(H):
+            cr, sr = ref[h]
+            orr, _, _ = oracle.head_step(oc, 0, h, int(hb[h]), cr, sr, q[0, h], k[0, h], v[0, h],
+                                         np.float32([alpha[0, h]]), float(dt[0, h]), step=t)
+            off = oracle.head_offset(oc, 0, h, hb)
+            assert np.array_equal(scales[0, h].view(np.uint32), sr.view(np.uint32))
+            assert np.array_equal(codes[off:off + cr.size], cr)
+            og = o.cpu().numpy().reshape(B, H, dv)[0, h]
+            assert np.allclose(og, orr, rtol=1e-4, atol=1e-37)
+    S = torch.empty(B * H * dv * dk, device="cuda")
+    st.store_fp32(S)
+    torch.cuda.synchronize()
+    Sg = S.cpu().numpy().reshape(B, H, dv, dk)
+    for h in range(H):
+        assert np.array_equal(Sg[0, h], oracle.head_dequantize(oc, int(hb[h]), *ref[h]))
+    st.close()
