@@ -116,6 +116,44 @@ def fp32_bytes(w) -> int:
     return per_head * w.B * w.H
 
 
+def fp32_accuracy(w, hb, Q, torch, batch: int = 8, checkpoints=(1, 64, 256, 1024)):
+    """Readouts of the quantized state against an FP32-state run of the same
+    recurrence and inputs: rel-L2 of o over all heads at the checkpoints.
+    Heads are independent, so a batch of `batch` rows of the workload's heads
+    (same per-head widths, inputs drawn fresh every step) stands for B."""
+    import workloads as W
+    wb = w.scaled(B=batch)
+    n = wb.B * wb.H
+
+    def dev(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    uniform = bool(np.all(hb == hb[:, :1]))
+    f = Q.QState(Q.Config(wb.B, wb.H, wb.dk, wb.dv, 16, wb.mixer, 0, True, None, 0, 0))
+    f.load_fp32(torch.zeros(n * wb.dv * wb.dk, device="cuda"))
+    for t in range(wb.warmup):
+        f.step(*map(dev, W.step_inputs(wb, t)))
+    S = torch.empty(n * wb.dv * wb.dk, device="cuda")
+    f.store_fp32(S)
+    qs = Q.QState(Q.Config(wb.B, wb.H, wb.dk, wb.dv, wb.G, wb.mixer, wb.rounding, False,
+                           hb[:, 0].tolist() if uniform else None, 0, 0, wb.axis,
+                           None if uniform else hb.tolist(), wb.window))
+    qs.load_fp32(S)
+    o_q = torch.empty(n * wb.dv, device="cuda")
+    o_f = torch.empty_like(o_q)
+    out = {}
+    for t in range(1, max(checkpoints) + 1):
+        inp = tuple(map(dev, W.step_inputs(wb, wb.warmup + t - 1)))
+        qs.step(*inp, o_q)
+        f.step(*inp, o_f)
+        if t in checkpoints:
+            out[str(t)] = float(torch.linalg.vector_norm(o_q - o_f) / torch.linalg.vector_norm(o_f))
+    qs.close()
+    f.close()
+    return {"rel_l2_o": out, "batch": wb.B, "heads": n,
+            "note": "quantized vs FP32 state, same warm-up state and inputs"}
+
+
 def cpu_baseline(w, hb, seconds: float):
     """The CPU reference on a sample of heads, one host thread per core (up to
     16): heads are independent, so each thread steps its own heads; the
@@ -308,6 +346,7 @@ def main():
     }
 
     if not args.no_extras:
+        result["accuracy_vs_fp32_state"] = fp32_accuracy(w, hb, Q, torch)
         ms_hot = timed(states[:1], args.steps, args.warmup)
         result["hot_single_state"] = {"ms_per_step": ms_hot, "steps_per_s": 1e3 / ms_hot,
                                       "effective_gbps": nbytes / (ms_hot * 1e-3) / 1e9}
