@@ -17,9 +17,10 @@
 //    sign bit of each byte/nibble (offset binary c + 2^(n-1)); the decayed
 //    value c*sa is then one fma(cu, sa, -2^(n-1)*sa), which is exactly the
 //    rounded product c*sa because the addend is exact;
-//  * stochastic rounding evaluates floor(S'*inv + R/2^16) as
-//    floor(fma(S', inv*2^16, R) / 2^16): the scaling by 2^16 is exact, so the
-//    code is byte 2 of floor(fma(...)), gathered with v_perm_b32;
+//  * stochastic rounding needs no float conversion of the random bits: one
+//    fma with 1.5*2^23 leaves N = rint(S'*inv*2^f) in the low bits of the
+//    result, one integer add of R16 (an SDWA half-word operand) forms
+//    N*2^(16-f) + R16, and the code is byte 2 of the sum (sr_word);
 //  * round-to-nearest adds 1.5*2^23 inside the fma, which leaves the rounded
 //    code in the low byte of the result.
 
@@ -81,18 +82,25 @@ __device__ __forceinline__ uint32_t xorshift32(uint32_t y) {
   return y;
 }
 
-// The 16 random 16-bit values R of one 16-element block, as floats: one
-// hashed seed and a walk of seven xorshift32 steps give the block's eight
-// 32-bit words (low half: even element, high half: odd element).
-__device__ __forceinline__ void block_r16(uint32_t key, uint32_t block, float* r) {
-  uint32_t w = fmix32(key ^ block);
-  w = w > 1u ? w : 1u;
+// The eight random words of one 16-element block: one hashed seed and a walk
+// of seven xorshift32 steps; word p carries R16 of element 2p (low half) and
+// of element 2p + 1 (high half).
+__device__ __forceinline__ void block_words(uint32_t key, uint32_t block, uint32_t* w) {
+  uint32_t x = fmix32(key ^ block);
+  x = x > 1u ? x : 1u;
 #pragma unroll
   for (int pr = 0; pr < 8; ++pr) {
-    if (pr) w = xorshift32(w);
-    r[2 * pr] = (float)(w & 0xFFFFu);
-    r[2 * pr + 1] = (float)(w >> 16);
+    if (pr) x = xorshift32(x);
+    // materialise the word, so that its low half reaches the adds as an SDWA
+    // operand rather than through a separate masked copy of the last xor
+    asm("" : "+v"(x));
+    w[pr] = x;
   }
+}
+
+// R16 of element j of a block from its words.
+__device__ __forceinline__ uint32_t r16_of(const uint32_t* w, int j) {
+  return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------------------
@@ -210,6 +218,45 @@ __device__ __forceinline__ void unpack16(const uint32_t* w, float* cu) {
   }
 }
 
+// The rounded products c*s of a lane's E codes (E = 16: four INT8 words;
+// E = 32: four INT4 words) with the scales s0 (first 16) and s1 (last 16).
+// INT4 takes a shortcut: an offset nibble cu = c + 8 in [0, 15], alone in a
+// byte, read as an OCP E4M3 code is exactly cu * 2^-9 (subnormals below 8,
+// the lowest normal binade from 8), so one packed FP8 conversion widens two
+// elements; fma(cu * 2^-9, s * 2^9, -8 s) has the exact product cu * s, as
+// fma(cu, s, -8 s) has (power-of-two scalings are exact for |s| < 2^118).
+template <int BITS, int E>
+__device__ __forceinline__ void dequant_lane(const uint32_t* w, float s0, float s1, float* d) {
+  constexpr float bias = (float)(1 << (BITS - 1));
+  const float nb0 = -bias * s0, nb1 = -bias * s1;
+  if constexpr (BITS == 8) {
+    unpack16<8>(w, d);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) d[j] = __builtin_fmaf(d[j], s0, nb0);
+  } else {
+    const float u0 = s0 * 512.0f, u1 = s1 * 512.0f;
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+      const uint32_t x = w[q] ^ 0x88888888u;
+      const uint32_t lo = x & 0x0F0F0F0Fu;         // elements 8q + 0, 2, 4, 6
+      const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // elements 8q + 1, 3, 5, 7
+      const auto e01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+      const auto e23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+      const auto o01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+      const auto o23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+      const float u = 8 * q < 16 ? u0 : u1, nb = 8 * q < 16 ? nb0 : nb1;
+      d[8 * q + 0] = __builtin_fmaf(e01[0], u, nb);
+      d[8 * q + 1] = __builtin_fmaf(o01[0], u, nb);
+      d[8 * q + 2] = __builtin_fmaf(e01[1], u, nb);
+      d[8 * q + 3] = __builtin_fmaf(o01[1], u, nb);
+      d[8 * q + 4] = __builtin_fmaf(e23[0], u, nb);
+      d[8 * q + 5] = __builtin_fmaf(o23[0], u, nb);
+      d[8 * q + 6] = __builtin_fmaf(e23[1], u, nb);
+      d[8 * q + 7] = __builtin_fmaf(o23[1], u, nb);
+    }
+  }
+}
+
 // Bytes [a.BP, b.BP, c.BP, d.BP] of four words.
 template <int BP>
 __device__ __forceinline__ uint32_t gather4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -236,12 +283,24 @@ __device__ __forceinline__ void pack16(const uint32_t* src, uint32_t* out) {
   }
 }
 
-// floor(x) as int32 in one instruction.
-__device__ __forceinline__ int32_t floor_i32(float x) {
-  int32_t r;
-  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
+// Stochastic rounding (semantics in include/qstate.h) of one element whose
+// y = fma(S', inv * 2^f, 1.5 * 2^23) has the bits 0x4B400000 + N, N =
+// rint(S' * inv * 2^f) (the fma rounds the exact product once, to an integer,
+// since |N| <= r 2^f < 2^22).  The result's byte 2 is the code
+// floor((N 2^(16-f) + R16) / 2^16): 4-bit codes (f = 16) take bits(y) + R16,
+// whose byte 2 carries an extra 0x40 that the nibble drops; 8-bit codes
+// (f = 15) take 2 bits(y) + R16 + 2^23, where 2 * 0x4B400000 + 2^23 leaves
+// bits 16..23 clear.
+template <bool IS8>
+__device__ __forceinline__ uint32_t sr_word(float y, uint32_t r16) {
+  const uint32_t yb = __float_as_uint(y);
+  if constexpr (IS8)
+    return yb + (yb + r16) + 0x00800000u;
+  else
+    return yb + r16;
 }
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
 // Requantize one 16-element chunk with inverse scale inv into 16 packed codes
 // (four words for INT8, two for INT4).  block: the chunk's 16-element block
@@ -254,21 +313,23 @@ __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t 
                                            uint32_t* out) {
   uint32_t src[16];
   if constexpr (RND == kSR) {
-    float R[16];
-    block_r16(key, block, R);
+    constexpr float scale_f = BITS == 8 ? 32768.0f : 65536.0f;  // 2^f
+    uint32_t w[8];
+    block_words(key, block, w);
+    float y[16];
     if (__builtin_expect(inv <= 0x1p100f, 1)) {
-      const float i16 = inv * 65536.0f;
+      const float inv_f = inv * scale_f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], i16, R[j]));
-    } else {  // groups of tiny magnitude, where inv * 2^16 could overflow
+      for (int j = 0; j < 16; ++j) y[j] = __builtin_fmaf(sp[j], inv_f, kMagic);
+    } else {  // groups of tiny magnitude, where inv * 2^f could overflow: same exact product
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv, R[j] * (1.0f / 65536.0f))) << 16;
+      for (int j = 0; j < 16; ++j) y[j] = __builtin_fmaf(sp[j] * scale_f, inv, kMagic);
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) src[j] = sr_word<BITS == 8>(y[j], r16_of(w, j));
     pack16<BITS, 2>(src, out);
   } else {
     // y = 1.5*2^23 + rint(S'*inv): the code sits in the low mantissa bits.
-    constexpr float kMagic = 12582912.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv, kMagic));
     if constexpr (RND == kBDR) {
@@ -294,6 +355,32 @@ __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t 
       }
     }
     pack16<BITS, 0>(src, out);
+  }
+}
+
+// Stochastic rounding of 16 elements with one inverse scale per element
+// (key-axis groups, per-block widths): word j gets code j in byte 2.  The
+// width is 8-bit when is8.
+__device__ __forceinline__ void sr16_cols(const float* sp, const float* inv16, uint32_t key,
+                                          uint32_t block, bool is8, uint32_t* src) {
+  uint32_t w[8];
+  block_words(key, block, w);
+  const float scale_f = is8 ? 32768.0f : 65536.0f;
+  float imax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) imax = fmaxf(imax, inv16[j]);
+  float y[16];
+  if (__builtin_expect(imax <= 0x1p100f, 1)) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = __builtin_fmaf(sp[j], inv16[j] * scale_f, kMagic);
+  } else {  // a tiny-magnitude group, where inv * 2^f could overflow: same exact product
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = __builtin_fmaf(sp[j] * scale_f, inv16[j], kMagic);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t r = r16_of(w, j);
+    src[j] = is8 ? sr_word<true>(y[j], r) : sr_word<false>(y[j], r);
   }
 }
 
@@ -384,23 +471,8 @@ __device__ __forceinline__ void quantize16_rt(const float* sp, const float* inv1
                                               bool is8, uint32_t* out) {
   uint32_t src[16];
   if constexpr (RND == kSR) {
-    float R[16];
-    block_r16(key, block, R);
-    float imax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) imax = fmaxf(imax, inv16[j]);
-    if (__builtin_expect(imax <= 0x1p100f, 1)) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j] * 65536.0f, R[j]));
-    } else {  // a tiny-magnitude group, where inv * 2^16 could overflow
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j], R[j] * (1.0f / 65536.0f)))
-                 << 16;
-    }
+    sr16_cols(sp, inv16, key, block, is8, src);
   } else {
-    constexpr float kMagic = 12582912.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv16[j], kMagic));
     if constexpr (RND == kBDR) {

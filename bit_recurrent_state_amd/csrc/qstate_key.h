@@ -43,24 +43,9 @@ __device__ __forceinline__ void quantize16_cols(const float* sp, const float* in
                                                 uint32_t* out) {
   uint32_t src[16];
   if constexpr (RND == kSR) {
-    float R[16];
-    block_r16(key, block, R);
-    float imax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) imax = fmaxf(imax, inv16[j]);
-    if (__builtin_expect(imax <= 0x1p100f, 1)) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j] * 65536.0f, R[j]));
-    } else {  // a tiny-magnitude group, where inv * 2^16 could overflow
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        src[j] = (uint32_t)floor_i32(__builtin_fmaf(sp[j], inv16[j], R[j] * (1.0f / 65536.0f)))
-                 << 16;
-    }
+    sr16_cols(sp, inv16, key, block, BITS == 8, src);
     pack16<BITS, 2>(src, out);
   } else {
-    constexpr float kMagic = 12582912.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv16[j], kMagic));
     if constexpr (RND == kBDR) {

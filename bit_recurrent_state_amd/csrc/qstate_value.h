@@ -37,7 +37,6 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
   constexpr bool SR = RND == kSR;
   using Gm = Geo<DK, BITS>;
   constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
-  constexpr float bias = (float)(1 << (BITS - 1));
   constexpr bool two_groups = G < E;  // INT4 with G = 16
   constexpr int LPG = two_groups ? 0 : G / E;
   constexpr int ngr = DK / G;
@@ -103,19 +102,13 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
       const uint32_t w[4] = {ring[k].raw.x, ring[k].raw.y, ring[k].raw.z, ring[k].raw.w};
       const float s_0 = ring[k].s0, s_1 = ring[k].s1, vrow = ring[k].v;
       float d[E];
-      unpack16<BITS>(w, d);
-      if constexpr (E == 32) unpack16<BITS>(w + 2, d + 16);
       // decayed dequantized values (exactly the rounded c*(s*alpha) / (c*s)*alpha_j)
       if constexpr (vector_decay(MIXER)) {
-        const float nb0 = -bias * s_0, nb1 = -bias * s_1;
+        dequant_lane<BITS, E>(w, s_0, s_1, d);
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-          d[j] = __builtin_fmaf(d[j], j < 16 ? s_0 : s_1, j < 16 ? nb0 : nb1) * al[j];
+        for (int j = 0; j < E; ++j) d[j] *= al[j];
       } else {
-        const float sa0 = s_0 * alpha_s, sa1 = s_1 * alpha_s;
-        const float nb0 = -bias * sa0, nb1 = -bias * sa1;
-#pragma unroll
-        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], j < 16 ? sa0 : sa1, j < 16 ? nb0 : nb1);
+        dequant_lane<BITS, E>(w, s_0 * alpha_s, s_1 * alpha_s, d);
       }
       // write weight
       float wt;

@@ -232,7 +232,6 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   using Gm = Geo<DK, BITS>;
   constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
   constexpr bool SR = RND == kSR;
-  constexpr float bias = (float)(1 << (BITS - 1));
   constexpr bool two_groups = G < E;
   constexpr int LPG = two_groups ? 0 : G / E;
   constexpr int ngr = DK / G;
@@ -319,18 +318,12 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
       uint32_t ab[4] = {0u, 0u, 0u, 0u};
       age_order<W>(ring[k].a, slot, ab);
       float d[E];
-      unpack16<BITS>(w, d);
-      if constexpr (E == 32) unpack16<BITS>(w + 2, d + 16);
       if constexpr (vector_decay(MIXER)) {
-        const float nb0 = -bias * s_0, nb1 = -bias * s_1;
+        dequant_lane<BITS, E>(w, s_0, s_1, d);
 #pragma unroll
-        for (int j = 0; j < E; ++j)
-          d[j] = __builtin_fmaf(d[j], j < 16 ? s_0 : s_1, j < 16 ? nb0 : nb1) * al[j];
+        for (int j = 0; j < E; ++j) d[j] *= al[j];
       } else {
-        const float sa0 = s_0 * alpha_s, sa1 = s_1 * alpha_s;
-        const float nb0 = -bias * sa0, nb1 = -bias * sa1;
-#pragma unroll
-        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(d[j], j < 16 ? sa0 : sa1, j < 16 ? nb0 : nb1);
+        dequant_lane<BITS, E>(w, s_0 * alpha_s, s_1 * alpha_s, d);
       }
       // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A); its key
       // is read from LDS each iteration rather than held in E registers

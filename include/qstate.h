@@ -48,7 +48,10 @@
  *      else s' = m / r (correctly rounded), inv = the largest float with
  *      inv * m <= r (r / m rounded toward zero), so |S' * inv| <= r.
  *   6. RTN: code = round-half-even(S'_ij * inv)   (exact product)
- *      SR:  code = floor(fma(S'_ij, inv, u_ij)), u_ij = R16_ij * 2^-16
+ *      SR:  x = S'_ij * inv (exact product) rounded to the nearest multiple
+ *           of 2^-f, ties to even, f = 16 for 4-bit and 15 for 8-bit codes;
+ *           code = floor(x + R16_ij * 2^-16).  Over R16 the mean code is
+ *           exactly x, within 2^-(f+1) of S'_ij * inv.
  *      No clamp is ever active: both stay within [-r, r].
  *      BDR ("Preserving Updates" abstract: reversed elements are rounded
  *      toward their update, with no extra storage): n = the RTN code,

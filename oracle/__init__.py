@@ -64,7 +64,7 @@ def lib():
             "oracle_dot": (f32, [_P, _P, i32]),
             "oracle_group_scale": (None, [f32, i32, _P, _P]),
             "oracle_round_rtn": (i32, [f32, f32]),
-            "oracle_round_sr": (i32, [f32, f32, u32]),
+            "oracle_round_sr": (i32, [f32, f32, u32, i32]),
             "oracle_round_bdr": (i32, [f32, f32, f32, f32, i32]),
             "oracle_codes_bytes": (ctypes.c_size_t, [cp, _P]),
             "oracle_head_offset": (ctypes.c_size_t, [cp, _P, i32, i32]),
@@ -186,8 +186,8 @@ def round_rtn(x: float, inv: float) -> int:
     return lib().oracle_round_rtn(x, inv)
 
 
-def round_sr(x: float, inv: float, r16: int) -> int:
-    return lib().oracle_round_sr(x, inv, r16)
+def round_sr(x: float, inv: float, r16: int, bits: int) -> int:
+    return lib().oracle_round_sr(x, inv, r16, bits)
 
 
 def round_bdr(x: float, inv: float, s_new: float, prev: float, r: int) -> int:

@@ -136,11 +136,17 @@ int oracle_round_rtn(float x, float inv) {
   return (int)std::rint((double)x * (double)inv);
 }
 
-// Stochastic rounding (LoReS 3/4, conditionally unbiased): floor(x*inv + u)
-// with u = r16 / 2^16, the sum formed by one fused multiply-add.
-int oracle_round_sr(float x, float inv, uint32_t r16) {
-  const float u = (float)(r16 & 0xFFFFu) * (1.0f / 65536.0f);
-  return (int)std::floor(std::fma(x, inv, u));
+// Stochastic rounding (LoReS 3/4, conditionally unbiased).  The exact
+// product x*inv is first rounded to the nearest multiple of 2^-f, ties to
+// even, with f = 16 fraction bits for 4-bit codes and 15 for 8-bit codes;
+// the code is floor(that + r16 / 2^16).  Over the 2^16 equally likely r16 the
+// mean code is exactly the f-bit value, within 2^-(f+1) of x*inv.  The double
+// product of two floats is exact, and so are the power-of-two scalings.
+int oracle_round_sr(float x, float inv, uint32_t r16, int bits) {
+  const int f = bits == 8 ? 15 : 16;
+  const double n = std::nearbyint(std::ldexp((double)x * (double)inv, f));
+  const double t = std::ldexp(n, 16 - f) + (double)(r16 & 0xFFFFu);
+  return (int)std::floor(t / 65536.0);
 }
 
 // Bounded directional rounding ("Preserving Updates", abstract: reversed
@@ -286,7 +292,8 @@ static void quantize_group(const oracle_cfg* c, const Layout& L, uint32_t key,
                            const std::vector<int64_t>& e, size_t si,
                            const float* S, const float* prev, uint8_t* codes,
                            float* scales, double* xval) {
-  const int r = qmax(L.bits[(int)(e[0] % c->dk) / 16]);
+  const int bits = L.bits[(int)(e[0] % c->dk) / 16];
+  const int r = qmax(bits);
   float m = 0.0f;
   for (int64_t x : e) m = std::max(m, std::fabs(S[x]));
   float s, inv;
@@ -296,11 +303,8 @@ static void quantize_group(const oracle_cfg* c, const Layout& L, uint32_t key,
     int n;
     if (c->rounding == kRoundSR) {
       const uint32_t r16 = oracle_sr_bits(key, (uint64_t)x);
-      n = oracle_round_sr(S[x], inv, r16);
-      if (xval) {
-        const float u = (float)r16 * (1.0f / 65536.0f);
-        xval[x] = (double)std::fma(S[x], inv, u);
-      }
+      n = oracle_round_sr(S[x], inv, r16, bits);
+      if (xval) xval[x] = (double)S[x] * (double)inv + (double)r16 / 65536.0;
     } else if (c->rounding == kRoundBDR && prev) {
       n = oracle_round_bdr(S[x], inv, s, prev[x], r);
       if (xval) xval[x] = (double)S[x] * (double)inv;

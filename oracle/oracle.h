@@ -55,7 +55,7 @@ uint32_t oracle_sr_bits(uint32_t key, uint64_t element);
 float oracle_dot(const float* x, const float* y, int n);
 void oracle_group_scale(float m, int r, float* s, float* inv);
 int oracle_round_rtn(float x, float inv);
-int oracle_round_sr(float x, float inv, uint32_t r16);
+int oracle_round_sr(float x, float inv, uint32_t r16, int bits);
 int oracle_round_bdr(float x, float inv, float s_new, float prev, int r);
 
 /* ---- layout ----
@@ -73,7 +73,7 @@ void oracle_set_code(uint8_t* head_codes, int bits, int64_t e, int code);
  * KDA) / dt (scalar), unused for GLA.
  * o, pre, xval may be NULL.  pre receives S' [dv][dk] before requantizing;
  * xval receives the pre-rounding value per element (RTN: the exact product
- * S'*inv; SR: fma(S', inv, u)). */
+ * S'*inv; SR: S'*inv + u, exact). */
 void oracle_head_step(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                       uint8_t* codes, float* scales, const float* q,
                       const float* k, const float* v, const float* alpha,

@@ -8,10 +8,15 @@ fmaf (no contraction) checks it exhaustively or on large random samples:
 2. Offset-binary dequantization: fma(c + 2^(b-1), sa, -2^(b-1)*sa) == RN(c*sa)
    for every code c and random (incl. subnormal) sa below 2^120, the library's
    supported state magnitude (beyond it 2^(b-1)*sa itself may overflow).
-3. Stochastic rounding via an exact 2^16 scaling:
-   floor(fma(x, inv*2^16, R)) >> 16 == floor(fma(x, inv, R*2^-16)).
+3. Stochastic rounding by integer addition: with y = fma(x, inv*2^f, 1.5*2^23)
+   (or fma(x*2^f, inv, 1.5*2^23) for huge inv), byte 2 of bits(y) + R (4-bit,
+   f = 16; low nibble) or of 2 bits(y) + R + 2^23 (8-bit, f = 15) is the code
+   floor((rint(x*inv*2^f) * 2^(16-f) + R) / 2^16), computed here in double.
 4. Round-to-nearest via the 1.5*2^23 constant: the low bits of
    fma(x, inv, 1.5*2^23) hold rint(x*inv) of the exact product when |x*inv| <= r.
+5. INT4 widening through FP8: a byte b in [0, 15] read as OCP E4M3 (decoded
+   here from the format's definition) is b * 2^-9, and
+   fma(b * 2^-9, s * 2^9, -8 s) == RN((b - 8) * s) for s below 2^118.
 """
 
 import os
@@ -72,16 +77,63 @@ int main(void){
       const float inv = inv_rz(m, r);
       const float x = (rnd() & 1 ? -1.0f : 1.0f) * m * (float)(rnd() & 0xffffff) / 16777216.0f;
       const uint32_t R = rnd() & 0xffffu;
-      const int a = ((int)floorf(fmaf(x, inv * 65536.0f, (float)R))) >> 16;
-      const int b = (int)floorf(fmaf(x, inv, (float)R * (1.0f / 65536.0f)));
-      if (a != b) { if (bad3 < 5) printf("sr x=%a inv=%a R=%u\n", x, inv, R); ++bad3; }
+      const int f = bits == 4 ? 16 : 15;
+      const float sf = (float)(1 << f);
+      const double nr = nearbyint(ldexp((double)x * (double)inv, f));
+      const int want = (int)floor((ldexp(nr, 16 - f) + (double)R) / 65536.0);
+      const uint32_t yb = u_of(fmaf(x, inv * sf, 12582912.0f));
+      const uint32_t yb2 = u_of(fmaf(x * sf, inv, 12582912.0f));
+      const uint32_t t = bits == 4 ? yb + R : yb + (yb + R) + 0x00800000u;
+      const int code = bits == 4 ? (int)(((t >> 16) & 0xFu) ^ 8u) - 8 : (int)(int8_t)(t >> 16);
+      if (code != want || yb != yb2 || abs(want) > (int)r) {
+        if (bad3 < 5) printf("sr x=%a inv=%a R=%u\n", x, inv, R); ++bad3; }
       const int n = (int)(u_of(fmaf(x, inv, 12582912.0f)) - 0x4B400000u);
       const int w = (int)rint((double)x * (double)inv);
       if (n != w || abs(w) > (int)r) { if (bad4 < 5) printf("rtn x=%a inv=%a\n", x, inv); ++bad4; }
     }
   }
-  printf("identity3 %ld\nidentity4 %ld\n", bad3, bad4);
-  return (bad || bad2 || bad3 || bad4) ? 1 : 0;
+  /* 3 for tiny groups (inv above 2^100): the scaled-x form */
+  for (int bits = 4; bits <= 8; bits += 4) {
+    const float r = (float)((1 << (bits - 1)) - 1);
+    const int f = bits == 4 ? 16 : 15;
+    const float sf = (float)(1 << f);
+    for (int it = 0; it < 1000000; ++it) {
+      const uint32_t e8 = rnd() % 24;  /* m from subnormal up to 2^-104 */
+      const float m = f_of((e8 << 23) | (rnd() & 0x7fffffu));
+      if (m == 0.0f) continue;
+      const float inv = inv_rz(m, r);
+      const uint32_t back = rnd() % 4096u;  /* |x| <= m, x stays a float below m */
+      const float x = (rnd() & 1 ? -1.0f : 1.0f) * f_of(u_of(m) - (back < u_of(m) ? back : 0u));
+      const uint32_t R = rnd() & 0xffffu;
+      const double nr = nearbyint(ldexp((double)x * (double)inv, f));
+      const int want = (int)floor((ldexp(nr, 16 - f) + (double)R) / 65536.0);
+      const uint32_t yb = u_of(fmaf(x * sf, inv, 12582912.0f));
+      const uint32_t t = bits == 4 ? yb + R : yb + (yb + R) + 0x00800000u;
+      const int code = bits == 4 ? (int)(((t >> 16) & 0xFu) ^ 8u) - 8 : (int)(int8_t)(t >> 16);
+      if (code != want || abs(want) > (int)r) {
+        if (bad3 < 10) printf("sr-tiny x=%a inv=%a R=%u\n", x, inv, R); ++bad3; }
+    }
+  }
+  /* 5 */
+  long bad5 = 0;
+  for (int b = 0; b < 16; ++b) {
+    const int e = b >> 3, mm = b & 7;
+    const double dec = e == 0 ? ldexp(mm, -9) : ldexp(1.0 + mm / 8.0, e - 7);
+    if (dec != ldexp(b, -9)) { printf("e4m3 b=%d\n", b); ++bad5; }
+  }
+  for (int it = 0; it < 200000; ++it) {
+    uint32_t u = rnd() & 0x7fffffffu;
+    if ((u >> 23) >= 245) u &= 0x3fffffffu;  /* s < 2^118 */
+    const float sa = f_of(u);
+    for (int b = 0; b < 16; ++b) {
+      const float got = fmaf(ldexpf((float)b, -9), sa * 512.0f, -8.0f * sa);
+      const float want = (float)(b - 8) * sa;
+      if (u_of(got) != u_of(want) && !(got == 0.0f && want == 0.0f)) {
+        if (bad5 < 5) printf("fp8deq b=%d sa=%a\n", b, sa); ++bad5; }
+    }
+  }
+  printf("identity3 %ld\nidentity4 %ld\nidentity5 %ld\n", bad3, bad4, bad5);
+  return (bad || bad2 || bad3 || bad4 || bad5) ? 1 : 0;
 }
 """
 
@@ -96,4 +148,5 @@ def test_kernel_float_identities():
         r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
         lines = dict(l.split() for l in r.stdout.splitlines() if l.startswith("identity"))
         assert r.returncode == 0, r.stdout
-        assert lines == {"identity1": "0", "identity2": "0", "identity3": "0", "identity4": "0"}
+        assert lines == {"identity1": "0", "identity2": "0", "identity3": "0", "identity4": "0",
+                         "identity5": "0"}

@@ -5,6 +5,7 @@ blog, Prop. "per-channel readout error"; 4/4 animation details), value-axis
 (row) groups (1/4), round-to-nearest and stochastic rounding (3/4), INT4 codes
 packed two per byte."""
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -100,19 +101,50 @@ def test_rtn_idempotent(oracle, bits):
 
 
 def test_sr_exhaustive_expectation(oracle):
-    """Averaging floor(x*inv + u) over all 65536 draws of u = R/2^16 reproduces
-    t = x*inv to within one draw step (conditional unbiasedness, 3/4)."""
+    """Over all 65536 draws R, the stochastic-rounding code averages exactly to
+    x*inv rounded to the nearest multiple of 2^-f (f = 16 for INT4, 15 for
+    INT8; ties to even), which is within 2^-(f+1) of x*inv: conditional
+    unbiasedness (3/4) up to that fixed resolution.  Exact rational
+    arithmetic, independent of the oracle's formula."""
     rng = np.random.default_rng(53)
     R = np.arange(65536)
-    for r in (7, 127):
-        for _ in range(6):
+    for bits, f in ((4, 16), (8, 15)):
+        r = 2 ** (bits - 1) - 1
+        for i in range(8):
             m = np.float32(abs(rng.standard_normal()) + 0.1)
             s, inv = oracle.group_scale(float(m), r)
-            x = np.float32(rng.uniform(-1, 1) * m)
-            t = float(Fraction(float(x)) * Fraction(float(inv)))
-            vals = np.array([oracle.round_sr(float(x), float(inv), int(rr)) for rr in R[::1]])
-            assert set(np.unique(vals)) <= {np.floor(t), np.floor(t) + 1}
-            assert abs(vals.mean() - t) <= 2.0**-15
+            x = np.float32(rng.uniform(-1, 1) * m) if i else np.float32(m)
+            t = Fraction(float(x)) * Fraction(float(inv))
+            tf = Fraction(round(t * 2 ** f), 2 ** f)  # Python's round: ties to even
+            assert abs(tf - t) <= Fraction(1, 2 ** (f + 1))
+            vals = np.array([oracle.round_sr(float(x), float(inv), int(rr), bits) for rr in R])
+            lo = math.floor(tf)
+            assert set(np.unique(vals).tolist()) <= {lo, lo + 1}
+            assert Fraction(int(vals.sum()), 65536) == tf
+            assert abs(vals).max() <= r
+
+
+def test_sr_threshold_and_ties(oracle):
+    """Hand cases of the SR definition: inv = 1 and x on the 2^-16 grid give
+    code = floor(x + R/2^16) exactly; the first rounding to 2^-f is
+    half-to-even (x = 2^-17 rounds to 0 for INT4, so every draw gives 0)."""
+    # x = 0.25: R < 49152 -> 0, R >= 49152 -> 1
+    assert oracle.round_sr(0.25, 1.0, 49151, 4) == 0
+    assert oracle.round_sr(0.25, 1.0, 49152, 4) == 1
+    # negative: x = -0.25 -> floor(-0.25 + R/2^16): R < 16384 -> -1
+    assert oracle.round_sr(-0.25, 1.0, 16383, 4) == -1
+    assert oracle.round_sr(-0.25, 1.0, 16384, 4) == 0
+    # ties at the 2^-16 (INT4) grid: 2^-17 -> 0, 3*2^-17 -> 2^-15 (even)
+    assert oracle.round_sr(2.0 ** -17, 1.0, 65535, 4) == 0
+    assert oracle.round_sr(3 * 2.0 ** -17, 1.0, 65534, 4) == 1
+    assert oracle.round_sr(3 * 2.0 ** -17, 1.0, 65533, 4) == 0
+    # INT8 rounds to the 2^-15 grid first: 2^-16 -> 0 (tie to even), 3*2^-16 -> 2^-14
+    assert oracle.round_sr(2.0 ** -16, 1.0, 65535, 8) == 0
+    assert oracle.round_sr(3 * 2.0 ** -16, 1.0, 65532, 8) == 1
+    assert oracle.round_sr(3 * 2.0 ** -16, 1.0, 65531, 8) == 0
+    # the ends of the range stay inside [-r, r]
+    assert oracle.round_sr(7.0, 1.0, 65535, 4) == 7
+    assert oracle.round_sr(-127.0, 1.0, 0, 8) == -127
 
 
 @pytest.mark.parametrize("bits", [4, 8])
