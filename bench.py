@@ -35,7 +35,7 @@ HBM_PEAK_GBPS = 8000.0
 ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", f)
-               for f in ("qstate_device.h", "qstate_value.h", "qstate_key.h")]
+               for f in ("qstate_device.h", "qstate_value.h", "qstate_persist.h", "qstate_key.h")]
 
 
 def kernel_source_hash() -> str:

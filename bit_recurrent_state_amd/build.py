@@ -3,8 +3,8 @@
 Each kernel source (one per dk and scale-group axis) and the host sources
 compile to objects in parallel under _build/, then link into the shared
 library.  Flags: no FP contraction (every fused multiply-add in the kernels
-is an explicit fmaf), IEEE-correct FP32 division, FP32 denormals kept, and
-packed FP32 instructions switched off.
+is an explicit fmaf), IEEE-correct FP32 division, FP32 denormals kept,
+packed FP32 instructions switched off, and no rewriting of atomics.
 """
 
 from __future__ import annotations
@@ -24,7 +24,8 @@ SOURCES = ([os.path.join(CSRC, f"qstate_window_dk{dk}_w{w}.hip")
            + [os.path.join(CSRC, "qstate_dispatch.cpp"), os.path.join(CSRC, "qstate_api.cpp")])
 HEADERS = [os.path.join(ROOT, "include", "qstate.h")] + [
     os.path.join(CSRC, h) for h in ("qstate_launch.h", "qstate_device.h", "qstate_value.h",
-                                    "qstate_key.h", "qstate_window.h")]
+                                    "qstate_key.h", "qstate_window.h",
+                                    "qstate_persist.h")]
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,6 +34,9 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a wave's work-unit claims are single-lane atomics whose results are
+    # read much later; the atomic optimizer would broadcast them at once
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -96,6 +96,7 @@ int check_config(const qstate_config* c) {
 
 uint64_t align16(uint64_t n) { return (n + 15) / 16 * 16; }
 
+
 // Bytes of one head's pure-write window area: a codes [dv][W], then two
 // copies of (b codes [W][dk], scales [W][2]).
 uint64_t window_head_bytes(const qstate_config* c) {
@@ -167,6 +168,37 @@ qs::KParams base_params(const qstate* s) {
     p.window = static_cast<uint8_t*>(s->state) + align16(s->bytes_per_b * s->cfg.batch);
   }
   return p;
+}
+
+// q = (mulhi(x, m) + x) >> s computes x / d for x < 2^31.
+qs::FastDiv fast_div(uint32_t d) {
+  qs::FastDiv f;
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  f.s = l;
+  f.m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+  return f;
+}
+
+// The persistent step's work units (value-axis heads of one width each, no
+// window): units of persist_unit_rows(dk) rows, INT8 heads first.
+void persist_params(const qstate* s, qs::KParams& p) {
+  const qstate_config& c = s->cfg;
+  if (c.fp32_state || c.group_axis != QSTATE_VALUE_AXIS || c.window != 0 || p.mixed) return;
+  const int uph = (c.dv + qs::persist_unit_rows(c.dk) - 1) / qs::persist_unit_rows(c.dk);
+  int n8 = 0;
+  for (int h = 0; h < c.heads; ++h)
+    if (s->int8_blocks[h] != 0) p.head_order[n8++] = (uint32_t)h;
+  int i = n8;
+  for (int h = 0; h < c.heads; ++h)
+    if (s->int8_blocks[h] == 0) p.head_order[i++] = (uint32_t)h;
+  p.persist = 1;
+  p.units_per_head = uph;
+  p.n_units = (uint32_t)((int64_t)c.batch * c.heads * uph);
+  p.n8_heads = n8;
+  p.div_uph = fast_div((uint32_t)uph);
+  p.div_n8 = fast_div((uint32_t)std::max(n8, 1));
+  p.div_n4 = fast_div((uint32_t)std::max(c.heads - n8, 1));
 }
 
 int run(const qstate* s, qs::Op op, const qs::KParams& p, void* stream) {
@@ -253,6 +285,7 @@ int qstate_step(qstate* s, const float* q, const float* k, const float* v, const
   p.alpha = alpha;
   p.beta = c.mixer == QSTATE_GLA ? nullptr : beta;
   p.o = o;
+  persist_params(s, p);
   const int rc = run(s, qs::kStep, p, stream);
   if (rc == QSTATE_OK) ++s->step;
   return rc;

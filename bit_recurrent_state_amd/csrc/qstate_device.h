@@ -163,15 +163,17 @@ __device__ __forceinline__ float lane_dot(const float (&x)[N], const float (&y)[
 
 // s = m / r, correctly rounded, as one product and one fused correction:
 // with c = RN(1/r), q = m*c, e = fma(-q, r, m), fma(e, c, q) equals RN(m/r)
-// for every normal m when r is 7 or 127 (an exhaustive check over all
-// mantissas is part of the tests); tiny m keeps the IEEE division.
+// for every m (subnormal results included) when r is 7 or 127, and for every
+// m >= 2^-100 when r is 448 (exhaustive checks over the mantissas are part of
+// the tests); r = 448 keeps the IEEE division below 2^-100.
 template <int R>
 __device__ __forceinline__ void group_scale(float m, float& s, float& inv) {
   constexpr float r = (float)R;
   constexpr float c = 1.0f / (float)R;
   const float q = m * c;
   s = __builtin_fmaf(__builtin_fmaf(-q, r, m), c, q);
-  if (__builtin_expect(m < 0x1p-100f && m != 0.0f, 0)) s = m / r;
+  if constexpr (R != 7 && R != 127)
+    if (__builtin_expect(m < 0x1p-100f && m != 0.0f, 0)) s = m / r;
   float v = r / m;
   if (__builtin_fmaf(m, v, -r) > 0.0f) v = __int_as_float(__float_as_int(v) - 1);
   inv = (m == 0.0f) ? 0.0f : v;
@@ -454,7 +456,6 @@ __device__ __forceinline__ void group_scale_rt(float m, bool is8, float& s, floa
   const float c = is8 ? 1.0f / 127.0f : 1.0f / 7.0f;
   const float q = m * c;
   s = __builtin_fmaf(__builtin_fmaf(-q, r, m), c, q);
-  if (__builtin_expect(m < 0x1p-100f && m != 0.0f, 0)) s = m / r;
   float v = r / m;
   if (__builtin_fmaf(m, v, -r) > 0.0f) v = __int_as_float(__float_as_int(v) - 1);
   inv = (m == 0.0f) ? 0.0f : v;
@@ -533,12 +534,22 @@ struct Slice {
   int head, b, h, r0, r1;
 };
 
+// The launch's workgroups are handed to the chip's 8 XCDs round-robin
+// (workgroup i to XCD i % 8).  In plain (b, h) order with H a multiple of 8,
+// head h of every batch row would land on XCD h % 8, and heads of different
+// widths (different costs) would load the XCDs unevenly.  Batch row b
+// therefore takes its heads rotated by b: workgroup position h0 in the row
+// runs head (h0 + b) mod H, so every XCD sees every head index, while the
+// workgroups in flight still cover one contiguous stretch of the state (the
+// HBM access pattern of the plain order).
 __device__ __forceinline__ Slice wave_slice(const KParams& p) {
   Slice sl;
-  sl.head = blockIdx.x / p.slices;
-  const int part = blockIdx.x - sl.head * p.slices;
-  sl.b = sl.head / p.H;
-  sl.h = sl.head - sl.b * p.H;
+  const int pos = blockIdx.x / p.slices;
+  const int part = blockIdx.x - pos * p.slices;
+  sl.b = pos / p.H;
+  const int h0 = pos - sl.b * p.H;
+  sl.h = (int)(((unsigned)h0 + (unsigned)sl.b) % (unsigned)p.H);
+  sl.head = sl.b * p.H + sl.h;
   sl.r0 = part * p.slice_rows;
   sl.r1 = min(p.dv, sl.r0 + p.slice_rows);
   return sl;

@@ -8,6 +8,12 @@
 
 namespace qs {
 
+// Division by a launch constant d: q = (mulhi(x, m) + x) >> s for x < 2^31,
+// with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1.
+struct FastDiv {
+  uint32_t m, s;
+};
+
 // Everything a kernel needs for one launch, passed by value.
 struct KParams {
   void* state;           // codes (quantized) or float S (FP32 state)
@@ -35,9 +41,21 @@ struct KParams {
   uint8_t* window;       // pure-write window areas of all heads, or null
   int32_t window_len;    // W: 0 (none), 4, 8 or 16
   uint64_t window_head_bytes;  // bytes of one head's window area
+  // Persistent value-axis step (persist != 0): work units of a fixed row
+  // count, INT8 heads first, then INT4 heads, each class in (b, h) order.
+  int32_t persist;
+  uint32_t n_units;            // B * H * units_per_head
+  int32_t units_per_head;
+  int32_t n8_heads;            // head indices h with INT8 width
+  FastDiv div_uph, div_n8, div_n4;  // by units_per_head, n8_heads, H - n8_heads
+  uint32_t head_order[256];    // the INT8 head indices, then the INT4 ones, ascending
 };
 
 enum Op { kStep = 0, kImport = 1, kExport = 2, kReadout = 3 };
+
+// Rows of one work unit of the persistent step: one trip of the INT4 load
+// ring (4 iterations of 64 / (dk / 32) rows).
+constexpr int persist_unit_rows(int dk) { return 4 * 64 / (dk / 32); }
 
 // Launch one kernel over all B*H heads on `stream`.  Returns hipSuccess or
 // the launch error.  mixer/rounding as in qstate.h; fp32 selects the

@@ -1,6 +1,6 @@
 // qstate_value_dk128.hip — value-axis and FP32-state kernels for dk = 128.
 
-#include "qstate_value.h"
+#include "qstate_persist.h"
 
 namespace qs {
 

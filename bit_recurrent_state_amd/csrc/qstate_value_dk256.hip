@@ -1,6 +1,6 @@
 // qstate_value_dk256.hip — value-axis and FP32-state kernels for dk = 256.
 
-#include "qstate_value.h"
+#include "qstate_persist.h"
 
 namespace qs {
 

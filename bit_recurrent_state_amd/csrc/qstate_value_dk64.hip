@@ -1,6 +1,6 @@
 // qstate_value_dk64.hip — value-axis and FP32-state kernels for dk = 64.
 
-#include "qstate_value.h"
+#include "qstate_persist.h"
 
 namespace qs {
 

@@ -4,7 +4,12 @@ exact IEEE-754 binary32 arithmetic, so a C program with correctly rounded
 fmaf (no contraction) checks it exhaustively or on large random samples:
 
 1. s = m / r for r in {7, 127, 448}: with c = RN(1/r), q = m*c, e = fma(-q, r, m),
-   fma(e, c, q) == RN(m / r) for every float mantissa (three exponent ranges).
+   fma(e, c, q) == RN(m / r) for every float mantissa (three exponent ranges),
+   and for r in {7, 127} also for every m below 2^-117: the subnormals and the
+   lowest binades, where q or the result is subnormal (above them every
+   quantity is normal and the check of one binade carries over by exact
+   power-of-two scaling), so these widths need no separate path for tiny
+   groups.
 2. Offset-binary dequantization: fma(c + 2^(b-1), sa, -2^(b-1)*sa) == RN(c*sa)
    for every code c and random (incl. subnormal) sa below 2^120, the library's
    supported state magnitude (beyond it 2^(b-1)*sa itself may overflow).
@@ -50,6 +55,15 @@ int main(void){
         const float got = fmaf(fmaf(-q, r, m), c, q);
         if (got != m / r) { if (bad < 5) printf("div r=%g m=%a\n", r, m); ++bad; }
       }
+  }
+  for (int t = 0; t < 2; ++t) {
+    const float r = rs[t], c = 1.0f / r;
+    for (uint32_t u = 1; u < (10u << 23); ++u) {
+      const float m = f_of(u);
+      const float q = m * c;
+      const float got = fmaf(fmaf(-q, r, m), c, q);
+      if (got != m / r) { if (bad < 5) printf("div-tiny r=%g m=%a\n", r, m); ++bad; }
+    }
   }
   printf("identity1 %ld\n", bad);
   /* 2 */
