@@ -4,7 +4,7 @@ Each kernel source (one per dk and scale-group axis) and the host sources
 compile to objects in parallel under _build/, then link into the shared
 library.  Flags: no FP contraction (every fused multiply-add in the kernels
 is an explicit fmaf), IEEE-correct FP32 division, FP32 denormals kept,
-packed FP32 instructions switched off, and no rewriting of atomics.
+and packed FP32 instructions switched off.
 """
 
 from __future__ import annotations
@@ -34,9 +34,6 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # a wave's work-unit claims are single-lane atomics whose results are
-    # read much later; the atomic optimizer would broadcast them at once
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
