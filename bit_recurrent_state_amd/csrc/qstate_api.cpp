@@ -196,7 +196,7 @@ void persist_params(const qstate* s, qs::KParams& p) {
   p.units_per_head = uph;
   p.n_units = (uint32_t)((int64_t)c.batch * c.heads * uph);
   p.n8_heads = n8;
-  p.div_uph = fast_div((uint32_t)uph);
+  p.div_group = fast_div((uint32_t)(8 * uph));
   p.div_n8 = fast_div((uint32_t)std::max(n8, 1));
   p.div_n4 = fast_div((uint32_t)std::max(c.heads - n8, 1));
 }

@@ -47,7 +47,7 @@ struct KParams {
   uint32_t n_units;            // B * H * units_per_head
   int32_t units_per_head;
   int32_t n8_heads;            // head indices h with INT8 width
-  FastDiv div_uph, div_n8, div_n4;  // by units_per_head, n8_heads, H - n8_heads
+  FastDiv div_group, div_n8, div_n4;  // by 8 * units_per_head, n8_heads, H - n8_heads
   uint32_t head_order[256];    // the INT8 head indices, then the INT4 ones, ascending
 };
 

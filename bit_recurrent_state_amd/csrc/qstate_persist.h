@@ -58,10 +58,18 @@ __device__ __forceinline__ PUnit decode_unit(const KParams& p, uint32_t u) {
   const uint32_t u8 = (uint32_t)p.B * n8 * (uint32_t)p.units_per_head;
   r.is8 = u < u8;
   const uint32_t v = r.is8 ? u : u - u8;
-  const uint32_t hi = fast_div(v, p.div_uph);  // head index inside the class
-  const uint32_t part = v - hi * (uint32_t)p.units_per_head;
-  const uint32_t bb = fast_div(hi, r.is8 ? p.div_n8 : p.div_n4);
   const uint32_t n = r.is8 ? n8 : (uint32_t)p.H - n8;
+  // Heads in groups of 8, each group's units ordered part-major: the units
+  // of one head lie 8 apart, so they go to waves on the same XCD (the chip
+  // hands workgroups to its 8 XCDs round-robin), whose L2 then serves the
+  // head's vectors to all of them.
+  const uint32_t uph = (uint32_t)p.units_per_head;
+  const uint32_t grp = fast_div(v, p.div_group);  // by 8 * units_per_head
+  const uint32_t rem = v - grp * 8u * uph;
+  const uint32_t hg = min(8u, (uint32_t)p.B * n - grp * 8u);  // heads in this group
+  const uint32_t part = hg == 8u ? rem >> 3 : rem / hg;
+  const uint32_t hi = grp * 8u + (rem - part * hg);  // head index inside the class
+  const uint32_t bb = fast_div(hi, r.is8 ? p.div_n8 : p.div_n4);
   r.b = (int)bb;
   r.h = p.head_order[(r.is8 ? 0u : n8) + hi - bb * n];
   r.r0 = (int)part * PGeo<DK>::UNIT_ROWS;
