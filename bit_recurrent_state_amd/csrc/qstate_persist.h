@@ -317,9 +317,14 @@ inline int device_cus() {
 }
 
 // Launch the persistent step: one wave per resident slot of the chip (or
-// one per unit when there are fewer units).
+// one per unit when there are fewer units).  It applies where the kernel
+// fits four waves per SIMD: with three, the grid of 3 waves per SIMD does
+// not divide the units of the usual shapes evenly (e.g. 8192 units over 3072
+// waves), and the waves left with an extra unit end alone; those kernels
+// (and states without a persistent layout) run the sliced step instead.
 template <int MIXER, int RND, int DK, int G>
-hipError_t launch_persist(const KParams& p, hipStream_t s) {
+bool launch_persist(const KParams& p, hipStream_t s, hipError_t* err) {
+  if (!p.persist) return false;
   static const int occ = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -328,12 +333,12 @@ hipError_t launch_persist(const KParams& p, hipStream_t s) {
       n = 0;
     return n;
   }();
-  int64_t waves = (int64_t)device_cus() * occ;
-  if (waves < 1) waves = 1024;  // no occupancy figure: any grid is correct
-  waves = std::min<int64_t>(waves, p.n_units);
-  if (waves < 1) return hipSuccess;  // no rows
+  if (occ < 16) return false;  // fewer than 4 waves per SIMD
+  const int64_t waves = std::min<int64_t>((int64_t)device_cus() * occ, p.n_units);
+  if (waves < 1) return false;
   step_persist_kernel<MIXER, RND, DK, G><<<(unsigned)waves, kThreads, 0, s>>>(p);
-  return hipGetLastError();
+  *err = hipGetLastError();
+  return true;
 }
 
 }  // namespace

@@ -14,11 +14,12 @@
 // lanes, the group absmax with DPP butterflies across the group's lanes.
 // Each state byte is read once and written once.
 //
-// Here: import / export / readout, the step of heads with mixed widths and
-// the FP32-state kernels, where one wave (a workgroup of 64 lanes) owns a
-// slice of the rows of one head (b, h) and small batches split a head into
-// several slices so that enough waves exist to fill 256 CUs.  The step of
-// heads of one width each is the persistent kernel of qstate_persist.h.
+// Here: import / export / readout, the step of heads with mixed widths, the
+// step of heads of one width where the persistent kernel of
+// qstate_persist.h does not apply, and the FP32-state kernels: one wave (a
+// workgroup of 64 lanes) owns a slice of the rows of one head (b, h), and
+// small batches split a head into several slices so that enough waves exist
+// to fill 256 CUs.
 
 #pragma once
 
@@ -33,6 +34,120 @@ struct RowIn {
   uint4 raw;
   float s0, s1, v;
 };
+
+// The step of one head slice of BITS-bit codes (heads of one width; the
+// kernels whose registers allow fewer than four waves per SIMD, where the
+// persistent step of qstate_persist.h cannot share out its units evenly).
+template <int MIXER, int RND, int DK, int BITS, int G>
+__device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl) {
+  constexpr bool SR = RND == kSR;
+  using Gm = Geo<DK, BITS>;
+  constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr bool two_groups = G < E;  // INT4 with G = 16
+  constexpr int LPG = two_groups ? 0 : G / E;
+  constexpr int ngr = DK / G;
+  const int lane = threadIdx.x;
+  const int lr = lane % LPR;
+  const int rsub = lane / LPR;
+  const int col0 = lr * E;
+  const int gcol = two_groups ? col0 / 16 : col0 / G;  // first group of the lane in its row
+
+  uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
+  float* hscales = p.scales + (size_t)sl.head * p.dv * ngr;
+  const float* vh = p.v + (size_t)sl.head * p.dv;
+  float* oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
+  const int n_it = (sl.r1 - sl.r0 + RPW - 1) / RPW;
+
+  // per-head vectors first, so that waiting for them never drains the ring
+  const uint32_t key = SR ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
+  float kk[E], qq[E], al[E];
+  loadv(p.k + (size_t)sl.head * DK + col0, kk);
+  loadv(p.q + (size_t)sl.head * DK + col0, qq);
+  float alpha_s = 0.0f, beta = 0.0f;
+  if constexpr (vector_decay(MIXER)) {
+    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) al[j] = 0.0f;
+    alpha_s = p.alpha[sl.head];
+  }
+  if constexpr (MIXER != kGLA) beta = p.beta[sl.head];
+  asm volatile("" ::: "memory");  // keep these loads ahead of the ring's
+
+  // Every lane always loads an in-range row: rows past the slice (the last
+  // iteration's tail and the prefetches beyond the end) re-read the slice's
+  // last row and are never stored.  Branch-free loads keep the ring's loads
+  // in flight across iterations.
+  auto load = [&](int it) {
+    RowIn in;
+    const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
+    in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+    in.s0 = hscales[(size_t)row * ngr + gcol];
+    in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
+    in.v = vh[row];
+    return in;
+  };
+  RowIn ring[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) {
+    ring[k] = load(k);
+    asm volatile("" ::: "memory");  // issue the slots in order: slot 0 is needed first
+  }
+
+  // Trips of kPrefetch iterations.  A slot's next load is issued once its
+  // previous contents (codes, scales, v) are dead, so the load lands in the
+  // same registers and stays in flight across trips.
+  // Iterations past the end compute on clamped rows and store nothing.
+  const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
+  for (int t = 0; t < n_trips; ++t) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int it = t * kPrefetch + k;
+      const int row = sl.r0 + it * RPW + rsub;
+      const bool store_ok = it < n_it && row < sl.r1;
+      const uint32_t w[4] = {ring[k].raw.x, ring[k].raw.y, ring[k].raw.z, ring[k].raw.w};
+      const float s_0 = ring[k].s0, s_1 = ring[k].s1, vrow = ring[k].v;
+      float d[E];
+      // decayed dequantized values (exactly the rounded c*(s*alpha) / (c*s)*alpha_j)
+      if constexpr (vector_decay(MIXER)) {
+        dequant_lane<BITS, E>(w, s_0, s_1, d);
+#pragma unroll
+        for (int j = 0; j < E; ++j) d[j] *= al[j];
+      } else {
+        dequant_lane<BITS, E>(w, s_0 * alpha_s, s_1 * alpha_s, d);
+      }
+      // write weight
+      float wt;
+      if constexpr (delta_rule(MIXER)) {
+        const float u = row_sum<LPR>(lane_dot(d, kk));
+        wt = beta * (vrow - u);
+      } else if constexpr (MIXER == kGLA) {
+        wt = vrow;
+      } else {
+        wt = beta * vrow;
+      }
+      // rank-1 write (in place) and readout from the full-precision S'
+#pragma unroll
+      for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+      ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
+      const float o = row_sum<LPR>(lane_dot(d, qq));
+      // requantize
+      float s0 = s_0, s1 = s_1;
+      const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
+      const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
+      if (store_ok) {
+        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        if constexpr (two_groups) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+          hscales[(size_t)row * ngr + gcol + 1] = s1;
+        } else if (lr % LPG == 0) {
+          hscales[(size_t)row * ngr + gcol] = s0;
+        }
+        if (oh && lr == 0) oh[row] = o;
+      }
+    }
+  }
+}
 
 // The same step on an unquantized FP32 head: 16 elements per lane.
 template <int MIXER, int DK>
@@ -385,11 +500,21 @@ __device__ __forceinline__ void aux_mixed_head(const KParams& p, const Slice sl)
 // ---------------------------------------------------------------------------
 
 // The step of a launch with heads of mixed widths: every head takes the
-// per-block path.  (Heads of one width each run the persistent step of
-// qstate_persist.h.)
+// per-block path.
 template <int MIXER, int RND, int DK, int G>
 __global__ __launch_bounds__(kThreads) void step_mixed_kernel(const KParams p) {
   step_mixed_head<MIXER, RND, DK, G>(p, wave_slice(p));
+}
+
+// The step of heads of one width each, one wave per head slice (when the
+// persistent step does not apply); the width is chosen per workgroup.
+template <int MIXER, int RND, int DK, int G>
+__global__ __launch_bounds__(kThreads) void step_sliced_kernel(const KParams p) {
+  const Slice sl = wave_slice(p);
+  if (p.int8_blocks[sl.h] != 0u)
+    step_quant_head<MIXER, RND, DK, 8, G>(p, sl);
+  else
+    step_quant_head<MIXER, RND, DK, 4, G>(p, sl);
 }
 
 template <int MIXER, int DK>
@@ -436,9 +561,10 @@ __global__ __launch_bounds__(kThreads) void readout_fp32_kernel(const KParams p)
 
 inline dim3 grid_of(const KParams& p) { return dim3((unsigned)(p.B * p.H * p.slices)); }
 
-// The persistent step of heads of one width each (qstate_persist.h).
+// The persistent step of heads of one width each (qstate_persist.h):
+// launches it and returns true, or returns false where it does not apply.
 template <int MIXER, int RND, int DK, int G>
-hipError_t launch_persist(const KParams& p, hipStream_t s);
+bool launch_persist(const KParams& p, hipStream_t s, hipError_t* err);
 
 template <int DK, int G, bool MIXED>
 hipError_t launch_quant(Op op, int mixer, int rnd, const KParams& p, hipStream_t s) {
@@ -455,13 +581,23 @@ hipError_t launch_quant(Op op, int mixer, int rnd, const KParams& p, hipStream_t
       }                                                                             \
       return hipGetLastError();                                                     \
     } else {                                                                        \
-      if (!p.persist) return hipErrorInvalidValue;                                  \
+      hipError_t e = hipSuccess;                                                    \
       switch (rnd) {                                                                \
-        case kRTN: return launch_persist<M, kRTN, DK, G>(p, s);                    \
-        case kSR: return launch_persist<M, kSR, DK, G>(p, s);                      \
-        case kBDR: return launch_persist<M, kBDR, DK, G>(p, s);                    \
+        case kRTN:                                                                  \
+          if (launch_persist<M, kRTN, DK, G>(p, s, &e)) return e;                   \
+          step_sliced_kernel<M, kRTN, DK, G><<<grid, block, 0, s>>>(p);             \
+          break;                                                                    \
+        case kSR:                                                                   \
+          if (launch_persist<M, kSR, DK, G>(p, s, &e)) return e;                    \
+          step_sliced_kernel<M, kSR, DK, G><<<grid, block, 0, s>>>(p);              \
+          break;                                                                    \
+        case kBDR:                                                                  \
+          if (launch_persist<M, kBDR, DK, G>(p, s, &e)) return e;                   \
+          step_sliced_kernel<M, kBDR, DK, G><<<grid, block, 0, s>>>(p);             \
+          break;                                                                    \
         default: return hipErrorInvalidValue;                                       \
       }                                                                             \
+      return hipGetLastError();                                                     \
     }                                                                               \
   }
     QS_STEP(kGDN) QS_STEP(kGLA) QS_STEP(kScalar) QS_STEP(kKDA)
