@@ -332,18 +332,29 @@ __device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
 // Kernels and dispatch.
 // ---------------------------------------------------------------------------
 
+// Heads of one width each.  Three waves per SIMD (at most 168 VGPRs, a few
+// spilled by the BDR and SR variants): the workgroup barriers of the column
+// reductions need the other waves to fill the SIMD, and measured, three
+// waves with spills beat two without by 8-12 %.
 template <int OP, int MIXER, int RND, int DK, int G>
-__global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_kernel(const KParams p) {
+__global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) __attribute__((amdgpu_waves_per_eu(3)))
+void key_kernel(const KParams p) {
   using K = KGeo<DK, G>;
   __shared__ float lds[K::LG * (K::PARTS + 3) * DK];
   const Slice sl = wave_slice(p);
-  const uint32_t m = p.int8_blocks[sl.h];
-  if (m == (1u << (DK / 16)) - 1u)
+  if (p.int8_blocks[sl.h] != 0u)
     key_quant_head<OP, MIXER, RND, DK, 8, G>(p, sl, lds);
-  else if (m == 0u)
-    key_quant_head<OP, MIXER, RND, DK, 4, G>(p, sl, lds);
   else
-    key_quant_head<OP, MIXER, RND, DK, 0, G>(p, sl, lds);
+    key_quant_head<OP, MIXER, RND, DK, 4, G>(p, sl, lds);
+}
+
+// A launch with heads of mixed widths: every head takes the per-block path
+// (held to three waves per SIMD, this path would spill heavily).
+template <int OP, int MIXER, int RND, int DK, int G>
+__global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_mixed_kernel(const KParams p) {
+  using K = KGeo<DK, G>;
+  __shared__ float lds[K::LG * (K::PARTS + 3) * DK];
+  key_quant_head<OP, MIXER, RND, DK, 0, G>(p, wave_slice(p), lds);
 }
 
 template <int OP, int DK, int G>
@@ -368,11 +379,20 @@ hipError_t launch_key(Op op, int mixer, int rnd, const KParams& p, hipStream_t s
     case kStep:
 #define QS_KSTEP(M)                                                                  \
   if (mixer == M) {                                                                  \
-    switch (rnd) {                                                                   \
-      case kRTN: key_kernel<kStep, M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
-      case kSR: key_kernel<kStep, M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
-      case kBDR: key_kernel<kStep, M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
-      default: return hipErrorInvalidValue;                                          \
+    if (p.mixed) {                                                                   \
+      switch (rnd) {                                                                 \
+        case kRTN: key_mixed_kernel<kStep, M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
+        case kSR: key_mixed_kernel<kStep, M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
+        case kBDR: key_mixed_kernel<kStep, M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
+        default: return hipErrorInvalidValue;                                        \
+      }                                                                              \
+    } else {                                                                         \
+      switch (rnd) {                                                                 \
+        case kRTN: key_kernel<kStep, M, kRTN, DK, G><<<grid, block, 0, s>>>(p); break; \
+        case kSR: key_kernel<kStep, M, kSR, DK, G><<<grid, block, 0, s>>>(p); break;   \
+        case kBDR: key_kernel<kStep, M, kBDR, DK, G><<<grid, block, 0, s>>>(p); break; \
+        default: return hipErrorInvalidValue;                                        \
+      }                                                                              \
     }                                                                                \
     return hipGetLastError();                                                        \
   }
@@ -380,10 +400,17 @@ hipError_t launch_key(Op op, int mixer, int rnd, const KParams& p, hipStream_t s
 #undef QS_KSTEP
       return hipErrorInvalidValue;
     case kImport:  // nothing stored before an import: BDR rounds to nearest
-      if (rnd == kSR)
-        key_kernel<kImport, kGDN, kSR, DK, G><<<grid, block, 0, s>>>(p);
-      else
-        key_kernel<kImport, kGDN, kRTN, DK, G><<<grid, block, 0, s>>>(p);
+      if (p.mixed) {
+        if (rnd == kSR)
+          key_mixed_kernel<kImport, kGDN, kSR, DK, G><<<grid, block, 0, s>>>(p);
+        else
+          key_mixed_kernel<kImport, kGDN, kRTN, DK, G><<<grid, block, 0, s>>>(p);
+      } else {
+        if (rnd == kSR)
+          key_kernel<kImport, kGDN, kSR, DK, G><<<grid, block, 0, s>>>(p);
+        else
+          key_kernel<kImport, kGDN, kRTN, DK, G><<<grid, block, 0, s>>>(p);
+      }
       return hipGetLastError();
     case kExport:
       key_aux_kernel<kExport, DK, G><<<grid, block, 0, s>>>(p);
