@@ -74,25 +74,26 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return h;
 }
 
-// Marsaglia's xorshift32, shifts 13, 17, 5.
-__device__ __forceinline__ uint32_t xorshift32(uint32_t y) {
-  y ^= y << 13;
-  y ^= y >> 17;
-  y ^= y << 5;
-  return y;
+// One step of the two 16-bit linear congruential streams of a word, x' =
+// (a x + c) mod 2^16 with a = 0xC36D in the low half and 0xC23D in the high
+// half, c = 13849 in both: one packed 16-bit multiply-add.
+__device__ __forceinline__ uint32_t lcg16x2(uint32_t w) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 a = {0xC36Du, 0xC23Du};
+  const u16x2 c = {13849u, 13849u};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) * a + c);
 }
 
-// The eight random words of one 16-element block: one hashed seed and a walk
-// of seven xorshift32 steps; word p carries R16 of element 2p (low half) and
-// of element 2p + 1 (high half).
+// The eight random words of one 16-element block: one hashed seed word and
+// seven steps of its linear congruential streams; word p carries R16 of
+// element 2p (low half) and of element 2p + 1 (high half).
 __device__ __forceinline__ void block_words(uint32_t key, uint32_t block, uint32_t* w) {
   uint32_t x = fmix32(key ^ block);
-  x = x > 1u ? x : 1u;
 #pragma unroll
   for (int pr = 0; pr < 8; ++pr) {
-    if (pr) x = xorshift32(x);
+    if (pr) x = lcg16x2(x);
     // materialise the word, so that its low half reaches the adds as an SDWA
-    // operand rather than through a separate masked copy of the last xor
+    // operand rather than through a separate masked copy
     asm("" : "+v"(x));
     w[pr] = x;
   }

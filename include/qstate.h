@@ -71,8 +71,10 @@
  *          g = 0x9E3779B97F4A7C15;  K = (uint32)(key >> 32) ^ (uint32)key.
  *   e = i*dk + j (element index within the head), block q = e / 16,
  *   pair p = (e % 16) / 2.
- *   z_q = max(fmix32(K ^ q), 1)          (MurmurHash3 32-bit finalizer)
- *   W   = xorshift32^p (z_q)             (Marsaglia 2003, shifts 13,17,5)
+ *   z_q = fmix32(K ^ q)                  (MurmurHash3 32-bit finalizer)
+ *   W   = L^p (z_q), where L steps the two 16-bit halves of a word as
+ *         linear congruential generators: low (0xC36D x + 13849) mod 2^16,
+ *         high (0xC23D x + 13849) mod 2^16 (each of full period 2^16).
  *   R16 = W & 0xFFFF for even e, W >> 16 for odd e.
  *  Each quantization event (a step, or an FP32 import) uses the handle's
  *  current step counter and then increments it.

@@ -58,7 +58,7 @@ def lib():
         sig = {
             "oracle_splitmix64_output": (u64, [u64]),
             "oracle_fmix32": (u32, [u32]),
-            "oracle_xorshift32": (u32, [u32]),
+            "oracle_lcg16x2": (u32, [u32]),
             "oracle_head_key": (u32, [u64, u32, u64, u32, u32]),
             "oracle_sr_bits": (u32, [u32, u64]),
             "oracle_dot": (f32, [_P, _P, i32]),
@@ -157,8 +157,8 @@ def fmix32(h: int) -> int:
     return lib().oracle_fmix32(h)
 
 
-def xorshift32(y: int) -> int:
-    return lib().oracle_xorshift32(y)
+def lcg16x2(w: int) -> int:
+    return lib().oracle_lcg16x2(w)
 
 
 def head_key(seed, layer, step, b, h) -> int:

@@ -59,12 +59,20 @@ uint32_t oracle_fmix32(uint32_t h) {
   return h;
 }
 
-// Marsaglia, "Xorshift RNGs", J. Stat. Softw. 8(14), 2003: shifts 13, 17, 5.
-uint32_t oracle_xorshift32(uint32_t y) {
-  y ^= y << 13;
-  y ^= y >> 17;
-  y ^= y << 5;
-  return y;
+// One step of the two 16-bit linear congruential streams that share a 32-bit
+// word (Lehmer's mixed generator x' = (a x + c) mod 2^16, one per half; Knuth,
+// TAOCP vol. 2, 3.2.1).  Low half a = 0xC36D, high half a = 0xC23D: both are
+// 5 mod 8, so with c odd each half has full period 2^16 (Hull-Dobell theorem),
+// and both were picked by the spectral test (TAOCP 3.3.4), with normalized
+// figures of merit of at least 0.75 in 2 to 5 dimensions.  c = 13849, about
+// (1/2 - sqrt(3)/6) 2^16, Knuth's increment for the smallest serial
+// correlation bound (TAOCP 3.3.3).
+uint32_t oracle_lcg16x2(uint32_t w) {
+  const uint32_t lo = w & 0xFFFFu;
+  const uint32_t hi = w >> 16;
+  const uint32_t lo_next = (0xC36Du * lo + 13849u) & 0xFFFFu;
+  const uint32_t hi_next = (0xC23Du * hi + 13849u) & 0xFFFFu;
+  return lo_next | (hi_next << 16);
 }
 
 // Per-(seed, layer, step, b, h) key: each field is absorbed through the
@@ -79,13 +87,13 @@ uint32_t oracle_head_key(uint64_t seed, uint32_t layer, uint64_t step,
 }
 
 // The 16 random bits of element e of a head: blocks of 16 elements share one
-// hashed seed, and the 8 element pairs of a block walk a xorshift32 stream.
+// hashed seed word, and the 8 element pairs of a block walk its two
+// linear congruential streams.
 uint32_t oracle_sr_bits(uint32_t key, uint64_t element) {
   const uint32_t block = (uint32_t)(element / 16);
   const int pair = (int)((element % 16) / 2);
   uint32_t w = oracle_fmix32(key ^ block);
-  if (w == 0) w = 1;  // xorshift32 never leaves 0
-  for (int p = 0; p < pair; ++p) w = oracle_xorshift32(w);
+  for (int p = 0; p < pair; ++p) w = oracle_lcg16x2(w);
   return (element % 2 == 0) ? (w & 0xFFFFu) : (w >> 16);
 }
 

@@ -46,7 +46,7 @@ typedef struct {
 /* ---- counter-based random bits ---- */
 uint64_t oracle_splitmix64_output(uint64_t z);
 uint32_t oracle_fmix32(uint32_t h);
-uint32_t oracle_xorshift32(uint32_t y);
+uint32_t oracle_lcg16x2(uint32_t w);
 uint32_t oracle_head_key(uint64_t seed, uint32_t layer, uint64_t step,
                          uint32_t b, uint32_t h);
 uint32_t oracle_sr_bits(uint32_t key, uint64_t element);

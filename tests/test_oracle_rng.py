@@ -45,50 +45,94 @@ def test_fmix32_is_a_bijection_sample(oracle):
     assert len(ys) == len(np.unique(xs))
 
 
-def _gf2_matrix(f):
-    """32x32 matrix over GF(2) of a linear map on 32-bit words (column j = f(e_j))."""
-    M = np.zeros((32, 32), dtype=np.uint8)
-    for j in range(32):
-        y = f(1 << j)
-        for i in range(32):
-            M[i, j] = (y >> i) & 1
-    return M
+M16 = 1 << 16
 
 
-def _matmul2(A, B):
-    return (A.astype(np.int64) @ B.astype(np.int64) % 2).astype(np.uint8)
+def _half_step(f, half):
+    """The map one half of a word takes under the word step f."""
+    if half == 0:
+        return lambda x: f(x) & 0xFFFF
+    return lambda x: f(x << 16) >> 16
 
 
-def _matpow2(A, e):
-    R = np.eye(32, dtype=np.uint8)
-    while e:
-        if e & 1:
-            R = _matmul2(R, A)
-        A = _matmul2(A, A)
-        e >>= 1
-    return R
-
-
-def test_xorshift32_linear_full_period(oracle):
-    # Marsaglia (2003): with a valid shift triple the xorshift32 map has
-    # period 2^32 - 1 on nonzero words, i.e. its GF(2) matrix T has order
-    # exactly 2^32 - 1 = 3*5*17*257*65537.  A wrong shift amount or direction
-    # breaks linearity or the order.
-    f = oracle.xorshift32
+def test_lcg16x2_halves_do_not_mix(oracle):
+    # Each half of the next word depends on the same half of the word only.
+    f = oracle.lcg16x2
     rng = np.random.default_rng(2)
-    for _ in range(200):
-        a, b = (int(x) for x in rng.integers(0, 2**32, 2, dtype=np.uint64))
-        assert f(a ^ b) == f(a) ^ f(b)
-    T = _gf2_matrix(f)
-    I = np.eye(32, dtype=np.uint8)
-    n = 2**32 - 1
-    assert np.array_equal(_matpow2(T, n), I)
-    for p in (3, 5, 17, 257, 65537):
-        assert not np.array_equal(_matpow2(T, n // p), I)
+    for _ in range(300):
+        lo, hi, lo2, hi2 = (int(x) for x in rng.integers(0, M16, 4))
+        w = f(lo | hi << 16)
+        assert w & 0xFFFF == f(lo | hi2 << 16) & 0xFFFF
+        assert w >> 16 == f(lo2 | hi << 16) >> 16
 
 
-def test_xorshift32_fixed_point_zero(oracle):
-    assert oracle.xorshift32(0) == 0
+@pytest.mark.parametrize("half", [0, 1])
+def test_lcg16x2_affine_and_full_period(oracle, half):
+    # Each half is a mixed linear congruential generator x -> (a x + c) mod
+    # 2^16 (a and c read off the values at 0 and 1, every other value then
+    # checked against them), with c odd and a = 1 mod 4 (Hull-Dobell), and
+    # its orbit from 0 visits all 2^16 values before it returns.
+    step = _half_step(oracle.lcg16x2, half)
+    c = step(0)
+    a = (step(1) - c) % M16
+    assert c % 2 == 1 and a % 4 == 1
+    seen = np.zeros(M16, dtype=bool)
+    x = 0
+    for _ in range(M16):
+        assert not seen[x]
+        seen[x] = True
+        y = step(x)
+        assert y == (a * x + c) % M16
+        x = y
+    assert x == 0 and seen.all()
+
+
+# Hermite constants gamma_t (exact for t <= 8).
+_GAMMA = {2: (4 / 3) ** 0.5, 3: 2 ** (1 / 3), 4: 2 ** 0.5, 5: 8 ** 0.2}
+
+
+def _spectral_merit(a, t):
+    """nu_t / (gamma_t^(1/2) m^(1/t)): nu_t is the length of the shortest
+    nonzero s with s_1 + a s_2 + ... + a^(t-1) s_t = 0 mod m (Knuth, TAOCP
+    vol. 2, 3.3.4), found by exhaustive search inside the bound that the
+    Hermite constant puts on it."""
+    m = M16
+    bound = int(np.ceil(_GAMMA[t] ** 0.5 * m ** (1 / t))) + 1
+    r = np.arange(-bound, bound + 1, dtype=np.int64)
+    grids = np.meshgrid(*([r] * (t - 1)), indexing="ij")
+    acc = np.zeros(grids[0].shape, dtype=np.int64)
+    sq = np.zeros_like(acc)
+    for i, g in enumerate(grids):
+        acc = (acc + pow(a, i + 1, m) * g) % m
+        sq += g * g
+    s1 = (-acc) % m
+    s1 = np.where(s1 > m // 2, s1 - m, s1)
+    n2 = sq + s1 * s1
+    n2 = np.where(n2 == 0, np.iinfo(np.int64).max, n2)
+    return float(np.sqrt(n2.min())) / (_GAMMA[t] ** 0.5 * m ** (1 / t))
+
+
+def test_spectral_merit_reference_values():
+    # Lattices worked by hand.  a = 1: the shortest dual vectors are
+    # (-1, 1) and (1, -1, 0), both of length sqrt 2.  a = 257 in three
+    # dimensions: 257^2 = 513 mod 2^16 and 1 - 2*257 + 513 = 0, so
+    # s = (1, -2, 1) of length sqrt 6, and no s with entries in [-2, 2] is
+    # shorter.
+    def nu(a, t):
+        return _spectral_merit(a, t) * _GAMMA[t] ** 0.5 * M16 ** (1 / t)
+    assert abs(nu(1, 2) - 2 ** 0.5) < 1e-9
+    assert abs(nu(1, 3) - 2 ** 0.5) < 1e-9
+    assert abs(nu(257, 3) - 6 ** 0.5) < 1e-9
+
+
+@pytest.mark.parametrize("half", [0, 1])
+def test_lcg16x2_multipliers_pass_spectral_test(oracle, half):
+    # Knuth's criterion for a good multiplier is a merit well above 0.1 in
+    # each dimension; these reach at least 0.75 in dimensions 2 to 5.
+    step = _half_step(oracle.lcg16x2, half)
+    a = (step(1) - step(0)) % M16
+    for t in (2, 3, 4, 5):
+        assert _spectral_merit(a, t) >= 0.75, (hex(a), t)
 
 
 def test_head_key_bits_balanced_and_avalanche(oracle):
@@ -119,7 +163,7 @@ def _head_bits(oracle, key, n):
 
 def test_sr_bits_uniform_and_uncorrelated(oracle):
     # 16-bit draws: uniform (chi-square on 64 bins) and no lag-1 correlation
-    # between neighbouring elements, across blocks and within the xorshift walk.
+    # between neighbouring elements, across blocks and within the block walk.
     vals = []
     for step in range(12):
         key = oracle.head_key(7, 1, step, 3, 5)
@@ -153,10 +197,15 @@ def test_sr_bits_independent_across_steps_and_heads(oracle):
 def test_sr_bits_block_structure(oracle):
     # Elements 2p and 2p+1 share one 32-bit word: low and high halves.
     key = oracle.head_key(1, 2, 3, 4, 5)
-    w0 = oracle.fmix32(key ^ 0) or 1
+    w0 = oracle.fmix32(key ^ 0)
     assert oracle.sr_bits(key, 0) == w0 & 0xFFFF
     assert oracle.sr_bits(key, 1) == w0 >> 16
-    w1 = oracle.xorshift32(w0)
+    w1 = oracle.lcg16x2(w0)
     assert oracle.sr_bits(key, 2) == w1 & 0xFFFF
-    w16 = oracle.fmix32(key ^ 1) or 1
+    assert oracle.sr_bits(key, 3) == w1 >> 16
+    w7 = w0
+    for _ in range(7):
+        w7 = oracle.lcg16x2(w7)
+    assert oracle.sr_bits(key, 15) == w7 >> 16
+    w16 = oracle.fmix32(key ^ 1)
     assert oracle.sr_bits(key, 16) == w16 & 0xFFFF
