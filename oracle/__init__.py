@@ -42,7 +42,8 @@ class Cfg(ctypes.Structure):
                 ("dv", ctypes.c_int32), ("G", ctypes.c_int32), ("mixer", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("layer", ctypes.c_uint32), ("axis", ctypes.c_int32),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("window_merge", ctypes.c_int32),
+                ("lrb_threshold", ctypes.c_float)]
 
 
 _lib = None
@@ -109,8 +110,9 @@ def _f32(a):
 
 
 def cfg(B, H, dk, dv, G, mixer=GDN, rounding=RTN, seed=0, layer=0, axis=VALUE_AXIS,
-        window=0) -> Cfg:
-    return Cfg(B, H, dk, dv, G, mixer, rounding, seed, layer, axis, window)
+        window=0, window_merge=0, lrb_threshold=0.5) -> Cfg:
+    return Cfg(B, H, dk, dv, G, mixer, rounding, seed, layer, axis, window, window_merge,
+               lrb_threshold)
 
 
 def scales_shape(c: Cfg):

@@ -458,6 +458,21 @@ void oracle_head_readout(const oracle_cfg* c, const uint8_t* block_bits, const u
 //
 // Window area of one head: a codes [dv][W], b codes [W][dk], then the scales
 // [W][2] (s_a, s_b), padded to a multiple of 16 bytes.
+//
+// Low-rank bypass ("Preserving Updates in Low-Bit Recurrent State
+// Quantization", abstract: small updates accumulate in a compact low-rank
+// buffer whose sufficiently large elements are merged into the state
+// periodically) uses the same buffer of W pairs with another merge rule.
+// Readings (the abstract gives no rank, period, threshold or format): the
+// buffer is the W most recent writes (rank <= W) in the pair format above,
+// propagated through the transition like the window; the period is W: the
+// step at a counter that is a multiple of W merges the whole buffer, every
+// element m_ij = sum over the pairs (oldest first) of a_i b'_j whose
+// magnitude reaches threshold * s_ig (s_ig the element's stored group scale
+// before the step) is added to the transitioned state, the others are
+// dropped, and the buffer is emptied; between merges the slot of the
+// counter is always empty, so those steps are the window step with an empty
+// leaving pair.
 // ---------------------------------------------------------------------------
 
 // OCP E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0 holds
@@ -559,7 +574,9 @@ void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block
   for (int i = 0; i < dv; ++i) anew[i] = (c->mixer == kMixerGLA) ? v[i] : beta * v[i];
   const float cnew = oracle_dot(k, q, dk);
 
-  // H' = H A + a_o b_o^T (the pair in `slot` leaves), o = H'q + window terms
+  // H' = H A + a_o b_o^T (the pair in `slot` leaves), o = H'q + window terms;
+  // a bypass merge step instead adds the buffer's large elements
+  const bool merge_all = c->window_merge == 1 && slot == 0;
   std::vector<float> d(dk), Sp((size_t)dv * dk), stored((size_t)dv * dk);
   const float* bo = Bp.data() + (size_t)slot * dk;
   for (int i = 0; i < dv; ++i) {
@@ -569,6 +586,21 @@ void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block
       const float s = scales[scale_index(c, i, j)];
       stored[(size_t)i * dk + j] = code * s;
       d[j] = vector_decay(c->mixer) ? (code * s) * alpha[j] : code * (s * alpha[0]);
+    }
+    if (merge_all) {
+      const float wh = delta ? -(beta * oracle_dot(d.data(), k, dk)) : 0.0f;
+      for (int j = 0; j < dk; ++j) {
+        const float t = delta ? std::fma(wh, k[j], d[j]) : d[j];
+        float m = 0.0f;
+        for (int age = 0; age < W; ++age) {
+          const int u = age_slot(c, step, age);
+          m = std::fma(A[(size_t)u * dv + i], Bp[(size_t)u * dk + j], m);
+        }
+        const float thr = c->lrb_threshold * scales[scale_index(c, i, j)];
+        sp[j] = std::fabs(m) >= thr ? t + m : t;
+      }
+      if (o) o[i] = std::fma(anew[i], cnew, oracle_dot(sp, q, dk));
+      continue;
     }
     const float ao = A[(size_t)slot * dv + i];
     if (delta) {
@@ -589,9 +621,17 @@ void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block
   if (pre) std::memcpy(pre, Sp.data(), sizeof(float) * Sp.size());
   quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, xval);
 
-  // store the window: propagated keys of the remaining pairs, the new pair
+  // store the window: propagated keys of the remaining pairs (after a bypass
+  // merge none remain), the new pair
   for (int t = 0; t < W; ++t) {
     if (t == slot) continue;
+    if (merge_all) {
+      for (int i = 0; i < dv; ++i) *win.acode(i, t) = 0;
+      for (int j = 0; j < dk; ++j) *win.bcode(t, j) = 0;
+      *win.scale(t, 0) = 0.0f;
+      *win.scale(t, 1) = 0.0f;
+      continue;
+    }
     fp8_vector(Bp.data() + (size_t)t * dk, dk, win.bcode(t, 0), 1, win.scale(t, 1));
   }
   fp8_vector(anew.data(), dv, win.acode(0, slot), (size_t)W, win.scale(slot, 0));

@@ -40,7 +40,12 @@ typedef struct {
   int32_t axis;     /* 0 value-axis groups (G key columns of one row, scales
                        [dv][dk/G]); 1 key-axis groups (G value rows of one
                        column, scales [dv/G][dk])                       */
-  int32_t window;   /* pure-write window length W (0: none)             */
+  int32_t window;   /* pair buffer length W (0: none)                   */
+  int32_t window_merge; /* 0 pure-write window: the oldest pair merges at
+                           every step; 1 low-rank bypass: every W steps all
+                           pairs merge, elements below the threshold drop */
+  float lrb_threshold;  /* low-rank bypass: an element merges when its
+                           magnitude is at least this times its group scale */
 } oracle_cfg;
 
 /* ---- counter-based random bits ---- */
