@@ -37,6 +37,7 @@ class QStateConfig(ctypes.Structure):
         ("head_bits", ctypes.POINTER(ctypes.c_uint8)), ("seed", ctypes.c_uint64),
         ("layer", ctypes.c_uint32), ("group_axis", ctypes.c_int32),
         ("channel_bits", ctypes.POINTER(ctypes.c_uint8)), ("window", ctypes.c_int32),
+        ("window_merge", ctypes.c_int32), ("lrb_threshold", ctypes.c_float),
     ]
 
 

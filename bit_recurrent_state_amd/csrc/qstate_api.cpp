@@ -8,6 +8,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -82,6 +83,10 @@ int check_config(const qstate_config* c) {
     // the window kernels take value-axis groups and heads of one width
     if (c->window != 4 && c->window != 8 && c->window != 16) return QSTATE_E_UNSUPPORTED;
     if (c->group_axis != QSTATE_VALUE_AXIS || c->channel_bits) return QSTATE_E_UNSUPPORTED;
+  }
+  if (c->window_merge != 0) {
+    if (c->window_merge != 1 || c->fp32_state || c->window == 0) return QSTATE_E_INVALID;
+    if (!(c->lrb_threshold >= 0.0f && c->lrb_threshold <= FLT_MAX)) return QSTATE_E_INVALID;
   }
   if (c->dk != 64 && c->dk != 128 && c->dk != 256) return QSTATE_E_UNSUPPORTED;
   if (c->heads > kMaxHeads || c->dv > kMaxDv) return QSTATE_E_UNSUPPORTED;
@@ -164,6 +169,8 @@ qs::KParams base_params(const qstate* s) {
   p.step = s->step;
   if (!s->cfg.fp32_state && s->cfg.window > 0) {
     p.window_len = s->cfg.window;
+    p.lrb_merge = s->cfg.window_merge == 1 && s->step % (uint64_t)s->cfg.window == 0;
+    p.lrb_theta = s->cfg.lrb_threshold;
     p.window_head_bytes = window_head_bytes(&s->cfg);
     p.window = static_cast<uint8_t*>(s->state) + align16(s->bytes_per_b * s->cfg.batch);
   }

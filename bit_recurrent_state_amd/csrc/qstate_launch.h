@@ -41,6 +41,8 @@ struct KParams {
   uint8_t* window;       // pure-write window areas of all heads, or null
   int32_t window_len;    // W: 0 (none), 4, 8 or 16
   uint64_t window_head_bytes;  // bytes of one head's window area
+  int32_t lrb_merge;     // low-rank bypass: this step merges the whole buffer
+  float lrb_theta;       // low-rank bypass: merge threshold, in group scales
   // Persistent value-axis step (persist != 0): work units of a fixed row
   // count, INT8 heads first, then INT4 heads, each class in (b, h) order.
   int32_t persist;

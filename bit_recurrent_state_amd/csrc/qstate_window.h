@@ -13,6 +13,14 @@
 // (counter + 1) & 1, so that waves sharing a head never see a half-written
 // key side; the a codes are partitioned by row and updated in place.
 //
+// Low-rank bypass ("Preserving Updates in Low-Bit Recurrent State
+// Quantization", abstract) runs in the same kernels: between merges its step
+// is the window step above (the leaving slot is empty then); at a counter
+// that is a multiple of W every pair's propagated key goes to LDS, each
+// element sums the W pairs' terms, keeps the sum where it reaches the
+// threshold times the element's stored scale, and the buffer empties but
+// for the new pair.
+//
 // Work split: the per-head window work (W*dk key elements) is spread over all
 // 64 lanes, 16 consecutive key columns of one pair per lane, with the same
 // 16-element chunks and DPP trees as the rows; every wave of a head does it
@@ -151,11 +159,16 @@ __device__ __forceinline__ void age_order(const ARow<W>& raw, int oldest, uint32
 // the new pair's c = k . q and a-side scale.  The writer (the head's first
 // slice) stores the propagated keys of the pairs that stay and the new
 // pair's key and scales into the written copy.
-template <int MIXER, int DK, int W>
+//
+// A low-rank bypass merge step (MERGE) instead puts every pair's
+// propagated key into LDS [W][dk] (lds_bo then points at W * dk floats) and
+// empties every slot but the new pair's.
+template <int MIXER, int DK, int W, bool MERGE>
 __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl, const WinHead& wh,
                                                 int slot, bool writer, float beta, float alpha_s,
                                                 float* lds_bo, float* lds_c, float* lds_sa,
                                                 float& c_new, float& s_anew, float& inv_anew) {
+  constexpr bool merge = MERGE;
   constexpr int LPP = DK / 16;         // lanes per pair
   constexpr int PPP = 64 / LPP;        // pairs per pass
   constexpr int PASSES = (W + PPP - 1) / PPP;
@@ -192,7 +205,12 @@ __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl
     const float c = row_sum<LPP>(chunk_dot(bp, q16, 0));
     if (act && lp == 0) lds_c[t] = c;
     const bool leaves = act && t == slot;
-    if (leaves) storev(lds_bo + c0, bp);
+    if constexpr (merge) {
+      if (act) storev(lds_bo + (size_t)t * DK + c0, bp);
+    } else if (leaves) {
+      storev(lds_bo + c0, bp);
+    }
+    const bool emptied = merge && act && t != slot;
     // stored key: b' for the pairs that stay, k for the new pair
     float x[16];
     float m = 0.0f;
@@ -209,10 +227,11 @@ __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl
     uint32_t w[4];
     fp8_pack16(x, w);
     if (writer && act) {
-      *reinterpret_cast<uint4*>(wh.b_wr + (size_t)t * DK + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(wh.b_wr + (size_t)t * DK + c0) =
+          emptied ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(w[0], w[1], w[2], w[3]);
       if (lp == 0) {
-        wh.s_wr[2 * t + 1] = s;
-        if (!leaves) wh.s_wr[2 * t] = wh.s_rd[2 * t];
+        wh.s_wr[2 * t + 1] = emptied ? 0.0f : s;
+        if (!leaves) wh.s_wr[2 * t] = emptied ? 0.0f : wh.s_rd[2 * t];
       }
     }
   }
@@ -227,7 +246,7 @@ __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl
   if (writer && lane == 0) wh.s_wr[2 * slot] = s_anew;
 }
 
-template <int MIXER, int RND, int DK, int BITS, int G, int W>
+template <int MIXER, int RND, int DK, int BITS, int G, int W, bool MERGE>
 __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, float* lds) {
   using Gm = Geo<DK, BITS>;
   constexpr int E = Gm::E, LPR = Gm::LPR, RPW = Gm::RPW;
@@ -278,11 +297,12 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
     ring[k] = load(k);
     asm volatile("" ::: "memory");
   }
-  float* lds_bo = lds;
-  float* lds_c = lds + DK;
+  float* lds_bo = lds;  // the leaving pair's key [dk], or every key [W][dk] (bypass merge)
+  float* lds_c = lds + W * DK;
   float* lds_sa = lds_c + W;
+  constexpr bool merge = MERGE;
   float c_new, s_anew, inv_anew;
-  window_prologue<MIXER, DK, W>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
+  window_prologue<MIXER, DK, W, MERGE>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
                                 lds_sa, c_new, s_anew, inv_anew);
   __syncthreads();
   float ca[W], sa[W];  // by age: 0 = oldest (leaving), W-1 = newest before this step
@@ -325,30 +345,61 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
       } else {
         dequant_lane<BITS, E>(w, s_0 * alpha_s, s_1 * alpha_s, d);
       }
-      // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A); its key
-      // is read from LDS each iteration rather than held in E registers
-      const float a_o = __builtin_amdgcn_cvt_f32_fp8((int)ab[0], 0) * sa[0];
-      float bo[E];
-      asm volatile("" ::: "memory");
-      loadv(lds_bo + col0, bo);
-      if constexpr (delta_rule(MIXER)) {
-        const float wt = -(beta * row_sum<LPR>(lane_dot(d, kk)));
-#pragma unroll
-        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(a_o, bo[j], __builtin_fmaf(wt, kk[j], d[j]));
-      } else {
-#pragma unroll
-        for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(a_o, bo[j], d[j]);
-      }
-      ring[k] = load(it + kPrefetch);
-      // readout of the full state: H'q, the pairs that stay (oldest first), the new pair
-      float o = row_sum<LPR>(lane_dot(d, qq));
-#pragma unroll
-      for (int g = 1; g < W; ++g) {
-        const float a_g = fp8_byte(ab[g >> 2], g & 3) * sa[g];
-        o = __builtin_fmaf(a_g, ca[g], o);
-      }
       const float a_new = MIXER == kGLA ? vrow : beta * vrow;
-      o = __builtin_fmaf(a_new, c_new, o);
+      float o;
+      if constexpr (merge) {
+        // bypass merge: H A, then the buffer's elements m = sum_g a_g b'_g (oldest
+        // first; slot 0 is the oldest here) that reach theta * the stored scale
+        if constexpr (delta_rule(MIXER)) {
+          const float wt = -(beta * row_sum<LPR>(lane_dot(d, kk)));
+#pragma unroll
+          for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
+        }
+        float m[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) m[j] = 0.0f;
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int g = 0; g < W; ++g) {
+          const float a_g = fp8_byte(ab[g >> 2], g & 3) * sa[g];
+          float bg[E];
+          loadv(lds_bo + (size_t)g * DK + col0, bg);
+#pragma unroll
+          for (int j = 0; j < E; ++j) m[j] = __builtin_fmaf(a_g, bg[j], m[j]);
+        }
+        const float thr0 = p.lrb_theta * s_0, thr1 = p.lrb_theta * s_1;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const float thr = (two_groups && j >= 16) ? thr1 : thr0;
+          d[j] = fabsf(m[j]) >= thr ? d[j] + m[j] : d[j];
+        }
+        ring[k] = load(it + kPrefetch);
+        o = __builtin_fmaf(a_new, c_new, row_sum<LPR>(lane_dot(d, qq)));
+      } else {
+        // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A); its
+        // key is read from LDS each iteration rather than held in E registers
+        const float a_o = __builtin_amdgcn_cvt_f32_fp8((int)ab[0], 0) * sa[0];
+        float bo[E];
+        asm volatile("" ::: "memory");
+        loadv(lds_bo + col0, bo);
+        if constexpr (delta_rule(MIXER)) {
+          const float wt = -(beta * row_sum<LPR>(lane_dot(d, kk)));
+#pragma unroll
+          for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(a_o, bo[j], __builtin_fmaf(wt, kk[j], d[j]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(a_o, bo[j], d[j]);
+        }
+        ring[k] = load(it + kPrefetch);
+        // readout of the full state: H'q, the pairs that stay (oldest first), the new pair
+        o = row_sum<LPR>(lane_dot(d, qq));
+#pragma unroll
+        for (int g = 1; g < W; ++g) {
+          const float a_g = fp8_byte(ab[g >> 2], g & 3) * sa[g];
+          o = __builtin_fmaf(a_g, ca[g], o);
+        }
+        o = __builtin_fmaf(a_new, c_new, o);
+      }
       float s0 = s_0, s1 = s_1;
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
       const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
@@ -363,7 +414,19 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
         if (lr == 0) {
           if (oh) oh[row] = o;
           const int code = __builtin_amdgcn_cvt_pk_fp8_f32(a_new * inv_anew, 0.0f, 0, false);
-          wh.a[(size_t)row * W + slot] = (uint8_t)(code & 0xFF);
+          if constexpr (merge) {  // the new pair in slot 0, the emptied slots zero
+            const uint32_t c0w = (uint32_t)code & 0xFFu;
+            uint8_t* arow = wh.a + (size_t)row * W;
+            if constexpr (W == 4) {
+              *reinterpret_cast<uint32_t*>(arow) = c0w;
+            } else if constexpr (W == 8) {
+              *reinterpret_cast<uint2*>(arow) = make_uint2(c0w, 0u);
+            } else {
+              *reinterpret_cast<uint4*>(arow) = make_uint4(c0w, 0u, 0u, 0u);
+            }
+          } else {
+            wh.a[(size_t)row * W + slot] = (uint8_t)(code & 0xFF);
+          }
         }
       }
     }
@@ -477,17 +540,19 @@ __device__ __forceinline__ void aux_pw_head(const KParams& p, const Slice sl, fl
 
 template <int DK, int W>
 constexpr int window_lds_floats() {
-  return (W * DK > DK + 2 * W) ? W * DK : DK + 2 * W;
+  return W * DK + 2 * W;
 }
 
-template <int MIXER, int RND, int DK, int G, int W>
+// MERGE: the low-rank bypass merge step (a kernel of its own, so that the
+// other steps keep the window kernel's registers).
+template <int MIXER, int RND, int DK, int G, int W, bool MERGE>
 __global__ __launch_bounds__(kThreads) void step_pw_kernel(const KParams p) {
   __shared__ float lds[window_lds_floats<DK, W>()];
   const Slice sl = wave_slice(p);
   if (p.int8_blocks[sl.h] != 0u)
-    step_pw_head<MIXER, RND, DK, 8, G, W>(p, sl, lds);
+    step_pw_head<MIXER, RND, DK, 8, G, W, MERGE>(p, sl, lds);
   else
-    step_pw_head<MIXER, RND, DK, 4, G, W>(p, sl, lds);
+    step_pw_head<MIXER, RND, DK, 4, G, W, MERGE>(p, sl, lds);
 }
 
 template <int OP, bool SR, int DK, int G, int W>
@@ -505,18 +570,24 @@ hipError_t launch_pw(Op op, int mixer, int rnd, const KParams& p, hipStream_t s)
   if (p.slice_rows % 32 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.B * p.H * p.slices)), block(kThreads);
   if (op == kStep) {
+#define QS_PW_R(M, R)                                                          \
+  if (p.lrb_merge)                                                             \
+    step_pw_kernel<M, R, DK, G, W, true><<<grid, block, 0, s>>>(p);            \
+  else                                                                         \
+    step_pw_kernel<M, R, DK, G, W, false><<<grid, block, 0, s>>>(p);
 #define QS_PW(M)                                                               \
   if (mixer == M) {                                                            \
     switch (rnd) {                                                             \
-      case kRTN: step_pw_kernel<M, kRTN, DK, G, W><<<grid, block, 0, s>>>(p); break; \
-      case kSR: step_pw_kernel<M, kSR, DK, G, W><<<grid, block, 0, s>>>(p); break;   \
-      case kBDR: step_pw_kernel<M, kBDR, DK, G, W><<<grid, block, 0, s>>>(p); break; \
+      case kRTN: QS_PW_R(M, kRTN) break;                                       \
+      case kSR: QS_PW_R(M, kSR) break;                                         \
+      case kBDR: QS_PW_R(M, kBDR) break;                                       \
       default: return hipErrorInvalidValue;                                    \
     }                                                                          \
     return hipGetLastError();                                                  \
   }
     QS_PW(kGDN) QS_PW(kGLA) QS_PW(kScalar) QS_PW(kKDA)
 #undef QS_PW
+#undef QS_PW_R
     return hipErrorInvalidValue;
   }
   switch (op) {

@@ -41,6 +41,8 @@ class Config:
     group_axis: int = VALUE_AXIS
     channel_bits: Optional[Sequence[Sequence[int]]] = None  # [heads][dk/16], overrides head_bits
     window: int = 0  # pure-write window length W (0, 4, 8 or 16)
+    window_merge: int = 0  # 0 pure-write window, 1 low-rank bypass (merge every W steps)
+    lrb_threshold: float = 0.5  # low-rank bypass: merge |m| >= threshold * group scale
 
     def to_c(self):
         """(QStateConfig, keep-alive buffers)."""
@@ -59,7 +61,8 @@ class Config:
             keep.append(cb)
         c = QStateConfig(self.batch, self.heads, self.dk, self.dv, self.group, self.mixer,
                          self.rounding, int(bool(self.fp32_state)), ptr, self.seed, self.layer,
-                         self.group_axis, cptr, self.window)
+                         self.group_axis, cptr, self.window, self.window_merge,
+                         self.lrb_threshold)
         return c, keep
 
     def bits(self) -> np.ndarray:

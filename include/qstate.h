@@ -114,6 +114,20 @@
  *      oldest first, then fma(a_new,i, dot(k, q), .);
  *   5. H' requantized as above; the kept pairs' b' and the new pair
  *      re-encoded.
+ * Low-rank bypass (window_merge = 1; "Preserving Updates in Low-Bit
+ * Recurrent State Quantization", abstract: small updates accumulate in a
+ * compact low-rank buffer whose sufficiently large elements are merged into
+ * the state periodically).  The buffer is the same W pairs (rank <= W),
+ * filled and propagated as above; the difference is the merge.  A step at a
+ * counter t with t mod W != 0 is the window step above (its slot is always
+ * empty then).  The step at t mod W == 0 merges the whole buffer instead:
+ *   m_ij = sum over the W pairs oldest first of fma(a_s,i, b'_s,j, m_ij)
+ *   from 0; T_ij = fma(-(beta * u_i), k_j, d_ij) with the delta rule, else
+ *   d_ij; H'_ij = T_ij + m_ij if |m_ij| >= lrb_threshold * s_ig (s_ig the
+ *   element's group scale before the step), else T_ij (the element drops);
+ *   o_i = fma(a_new,i, dot(k, q), dot(H'_i, q)); the new pair takes slot 0
+ *   and every other slot is emptied (zero codes and scales).
+ *
  * Window area per head (after the codes, 16-byte aligned, heads in (b, h)
  * order, each align16(dv*W + 2*(W*dk + 8*W)) bytes): a codes [dv][W], then two
  * copies of (b codes [W][dk], scales [W][2] = (s_a, s_b)); counter t reads
@@ -199,6 +213,13 @@ typedef struct {
                                low-bit state (value-axis groups, heads of one
                                width); their area follows the codes in the
                                codes buffer (see the pure-write window below) */
+  int32_t window_merge;     /* with W > 0: 0 = pure-write window (the oldest
+                               pair merges at every step); 1 = low-rank bypass
+                               (every W steps the whole buffer merges, see
+                               below)                                         */
+  float lrb_threshold;      /* low-rank bypass: a buffer element merges when
+                               its magnitude is at least this times its group
+                               scale; finite, >= 0 (0 merges every element)  */
 } qstate_config;
 
 typedef struct qstate qstate; /* opaque; host-side metadata only */

@@ -118,9 +118,10 @@ class Run:
         uniform = bool(np.all(self.bb == self.bb[:, :1]))
         self.cfg = Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, False,
                             [int(x) for x in self.bb[:, 0]] if uniform else None, seed, layer,
-                            w.axis, None if uniform else self.bb.tolist(), w.window)
+                            w.axis, None if uniform else self.bb.tolist(), w.window,
+                            w.window_merge, w.lrb_threshold)
         self.ocfg = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, self.rounding, seed, layer,
-                               w.axis, w.window)
+                               w.axis, w.window, w.window_merge, w.lrb_threshold)
         all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
         self.heads = all_heads if heads is None else list(heads)
         self.rep = Report()

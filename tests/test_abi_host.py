@@ -120,6 +120,26 @@ def test_window_rules_and_size(L):
         assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == st, kw
 
 
+def test_bypass_rules(L):
+    """The low-rank bypass needs a window and a finite threshold >= 0; it
+    keeps the window's area."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    c = _cfg(window=8)
+    assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+    pw_bytes = cb.value
+    for thr in (0.0, 0.5, 3.0):
+        c = _cfg(window=8, window_merge=1, lrb_threshold=thr)
+        assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == 0
+        assert cb.value == pw_bytes
+    for kw in (dict(window=0, window_merge=1), dict(window=8, window_merge=2),
+               dict(window=8, window_merge=-1), dict(window=8, window_merge=1, lrb_threshold=-0.5),
+               dict(window=8, window_merge=1, lrb_threshold=float("inf")),
+               dict(window=8, window_merge=1, lrb_threshold=float("nan")),
+               dict(window=8, window_merge=1, fp32_state=1)):
+        c = _cfg(**kw)
+        assert L.qstate_state_bytes(ctypes.byref(c), ctypes.byref(cb), ctypes.byref(sb)) == -1, kw
+
+
 def test_bad_head_bits_and_pointers(L):
     keep, hb = _bits(4, 6, 8)
     c = _cfg(head_bits=hb)

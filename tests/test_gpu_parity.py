@@ -188,6 +188,39 @@ def test_window_full_size_sampled_heads():
     _run(w, 10, heads=sorted((i // w.H, i % w.H) for i in idx))
 
 
+BYPASS_RUNS = [(2, W.SR, 8, 0.5), (3, W.RTN, 4, 0.5), (5, W.BDR, 16, 0.5), (4, W.SR, 8, 0.0),
+               (1, W.RTN, 4, 2.0), (3, W.SR, 16, 0.25)]
+
+
+@pytest.mark.parametrize("wid,rounding,window,theta", BYPASS_RUNS)
+def test_bypass_every_head(wid, rounding, window, theta):
+    """Low-rank bypass: state, buffer pairs and scales bit-exact at every step
+    across two merges, the readout and the exported full state."""
+    w = W.WORKLOADS[wid].scaled(B=2, window=window, window_merge=1, lrb_threshold=theta)
+    _run(w, 2 * window + 3, rounding=rounding)
+
+
+def test_bypass_heads_split_over_waves():
+    w = W.WORKLOADS[0].scaled(window=8, window_merge=1, dv=128, steps=20)
+    r = _run(w, 20)
+    assert r.steps == 20
+
+
+@pytest.mark.parametrize("mixer,rounding,dk,dv,G,bits,window", WINDOW_RAGGED)
+def test_bypass_shapes(mixer, rounding, dk, dv, G, bits, window):
+    w = W.Workload(75 + mixer, f"lrb_m{mixer}_dk{dk}_dv{dv}_g{G}_w{window}", mixer, 3, len(bits),
+                   dk, dv, G, 2 * window + 2, 3, rounding, "int8", window=window,
+                   window_merge=1, lrb_threshold=0.5)
+    _run(w, 2 * window + 2, hb=np.array(bits, np.uint8), seed=19)
+
+
+def test_bypass_full_size_sampled_heads():
+    w = W.WORKLOADS[2].scaled(window=8, window_merge=1)
+    rng = np.random.default_rng(43)
+    idx = set(rng.choice(w.B * w.H, 10, replace=False).tolist()) | {0, w.B * w.H - 1}
+    _run(w, 10, heads=sorted((i // w.H, i % w.H) for i in idx))
+
+
 @pytest.mark.parametrize("layer", [0, 5])
 def test_config4_scalar_decay_layers(layer):
     _run(W.WORKLOADS[4].scaled(B=3), 8, layer=layer)

@@ -47,7 +47,9 @@ class Workload:
     bits_policy: str     # "int8" | "alpha_gt_0.99" | "rank_half" | "channel_half"
     layers: int = 1
     axis: int = 0        # scale groups: 0 value axis (G key columns), 1 key axis (G value rows)
-    window: int = 0      # pure-write window length W (0: none)
+    window: int = 0      # pair buffer length W (0: none)
+    window_merge: int = 0  # 0 pure-write window, 1 low-rank bypass (merge every W steps)
+    lrb_threshold: float = 0.5  # low-rank bypass: merge threshold in group scales
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
