@@ -54,7 +54,8 @@ def kernel_source_hash() -> str:
 
 def traffic_key(w) -> str:
     key = f"{w.name}|{ROUNDING_NAMES[w.rounding]}|{'key' if w.axis else 'value'}-axis"
-    return key + (f"|window{w.window}" if w.window else "")
+    key += f"|window{w.window}" if w.window else ""
+    return key + ("|lrb" if w.window_merge else "")
 
 
 def measured_traffic(w):
@@ -106,9 +107,11 @@ def algorithmic_bytes(w, bb) -> int:
         if w.window:  # pure-write window: a codes read + the new pair's, keys and scales
             W = w.window
             per_b += w.dv * W + w.dv + 2 * (W * w.dk + 8 * W)
+            if w.window_merge:  # bypass: a merge step (1 in W) rewrites every a code of a row
+                per_b += w.dv * (W - 1) / W
         io = 4 * (2 * w.dk + 2 * w.dv)
         per_b += 2 * state + io + gate_bytes(w)
-    return per_b * w.B
+    return int(round(per_b * w.B))
 
 
 def fp32_bytes(w) -> int:
@@ -137,7 +140,8 @@ def fp32_accuracy(w, hb, Q, torch, batch: int = 8, checkpoints=(1, 64, 256, 1024
     f.store_fp32(S)
     qs = Q.QState(Q.Config(wb.B, wb.H, wb.dk, wb.dv, wb.G, wb.mixer, wb.rounding, False,
                            hb[:, 0].tolist() if uniform else None, 0, 0, wb.axis,
-                           None if uniform else hb.tolist(), wb.window))
+                           None if uniform else hb.tolist(), wb.window, wb.window_merge,
+                           wb.lrb_threshold))
     qs.load_fp32(S)
     o_q = torch.empty(n * wb.dv, device="cuda")
     o_f = torch.empty_like(o_q)
@@ -164,7 +168,8 @@ def cpu_baseline(w, hb, seconds: float):
     import workloads as W
 
     rng = np.random.default_rng(0)
-    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0, w.axis, w.window)
+    c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0, w.axis, w.window,
+                   w.window_merge, w.lrb_threshold)
     q, k, v, alpha, beta = W.step_inputs(w, 0)
     heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096), rng.integers(0, w.H, 4096))]
     S0 = rng.standard_normal((w.dv, w.dk)).astype(np.float32)
@@ -237,6 +242,8 @@ def main():
                     help="scale groups: 0 value axis (default), 1 key axis")
     ap.add_argument("--window", type=int, default=0,
                     help="pure-write window length (0 = none, 4, 8, 16)")
+    ap.add_argument("--lrb", type=float, default=None, metavar="THRESHOLD",
+                    help="low-rank bypass with this merge threshold (needs --window)")
     ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
     ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
     ap.add_argument("--cpu-seconds", type=float, default=1.5,
@@ -262,6 +269,11 @@ def main():
     if args.rounding is not None:
         w = w.scaled(rounding=args.rounding)
     w = w.scaled(axis=args.axis, window=args.window)
+    if args.lrb is not None:
+        if not args.window:
+            print(json.dumps({"error": "--lrb needs --window"}))
+            sys.exit(2)
+        w = w.scaled(window_merge=1, lrb_threshold=args.lrb)
     hb = block_bits(w, Q)  # [H][dk/16]
     uniform = bool(np.all(hb == hb[:, :1]))
     nbytes = algorithmic_bytes(w, hb)
@@ -269,7 +281,8 @@ def main():
     def qcfg(layer):
         return Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False,
                         hb[:, 0].tolist() if uniform else None, 0, layer, w.axis,
-                        None if uniform else hb.tolist(), w.window)
+                        None if uniform else hb.tolist(), w.window, w.window_merge,
+                        w.lrb_threshold)
 
     cfg0 = qcfg(0)
     cb, sb = Q.qstate_state_bytes(cfg0)
@@ -335,6 +348,7 @@ def main():
                             for b in sorted(set(hb.ravel().tolist()))}),
             "rounding": ROUNDING_NAMES[w.rounding],
             "group_axis": "key" if w.axis else "value", "window": w.window,
+            **({"low_rank_bypass_threshold": w.lrb_threshold} if w.window_merge else {}),
             "state_instances": n_states,
             "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,
         },
