@@ -93,7 +93,7 @@ def block_bits(w, Q) -> np.ndarray:
                          for h in range(w.H)]).astype(np.uint8)
     policy = {"alpha_gt_0.99": (0, 0.99), "rank_half": (1, 0.5)}.get(w.bits_policy)
     hb = (Q.qstate_bits_by_decay(W.head_retention(w), *policy) if policy
-          else np.full(w.H, 8, np.uint8))
+          else np.full(w.H, 4 if w.bits_policy == "int4" else 8, np.uint8))
     return np.repeat(hb[:, None], nb, axis=1).astype(np.uint8)
 
 
@@ -244,6 +244,9 @@ def main():
                     help="pure-write window length (0 = none, 4, 8, 16)")
     ap.add_argument("--lrb", type=float, default=None, metavar="THRESHOLD",
                     help="low-rank bypass with this merge threshold (needs --window)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch B")
+    ap.add_argument("--bits", choices=["int4", "int8"], default=None,
+                    help="override the per-head width policy: every head INT4 or INT8")
     ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
     ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
     ap.add_argument("--cpu-seconds", type=float, default=1.5,
@@ -269,6 +272,10 @@ def main():
     if args.rounding is not None:
         w = w.scaled(rounding=args.rounding)
     w = w.scaled(axis=args.axis, window=args.window)
+    if args.batch:
+        w = w.scaled(B=args.batch)
+    if args.bits:
+        w = w.scaled(bits_policy=args.bits)
     if args.lrb is not None:
         if not args.window:
             print(json.dumps({"error": "--lrb needs --window"}))

@@ -240,9 +240,9 @@ __device__ __forceinline__ void dequant_lane(const uint32_t* w, float s0, float 
     const float u0 = s0 * 512.0f, u1 = s1 * 512.0f;
 #pragma unroll
     for (int q = 0; q < E / 8; ++q) {
-      const uint32_t x = w[q] ^ 0x88888888u;
-      const uint32_t lo = x & 0x0F0F0F0Fu;         // elements 8q + 0, 2, 4, 6
-      const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // elements 8q + 1, 3, 5, 7
+      // offset nibbles c + 8 = c ^ 8, each alone in a byte (one bitop3 each)
+      const uint32_t lo = (w[q] & 0x0F0F0F0Fu) ^ 0x08080808u;         // elements 8q + 0, 2, 4, 6
+      const uint32_t hi = ((w[q] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;  // elements 8q + 1, 3, 5, 7
       const auto e01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
       const auto e23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
       const auto o01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
