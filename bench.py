@@ -255,7 +255,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "bench.py measures one GPU (heads shard across GPUs with no exchange); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -49,7 +49,7 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() or "
+        raise ImportError(f"{LIB_PATH} is not built: run "
                           "python -m bit_recurrent_state_amd.build")
     L = ctypes.CDLL(LIB_PATH)
     P, c_int, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
