@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.fixture(scope="module")
 def L():
     from bit_recurrent_state_amd import build
-    if build.stale():
+    if not os.path.exists(build.LIB):
         build.build()
     from bit_recurrent_state_amd._lib import lib
     return lib()
