@@ -23,7 +23,7 @@
  *    Gated DeltaNet, GLA, Mamba2 and RetNet as the recurrences in question,
  *    with savings measured against FP32 states.
  *
- * Semantics (exact, shared with the CPU checker; every FP32 operation below
+ * Semantics (exact, shared with the CPU reference; every FP32 operation below
  * is one IEEE-754 binary32 operation with round-to-nearest-even unless noted):
  *
  *  Per head (b,h) with bit width n (4 or 8), r = 2^(n-1) - 1, and per value
