@@ -167,10 +167,10 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       if constexpr (OP == kStep) {
         const uint8_t* src = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
         if (lc.is8) {
-          const uint4 t = *reinterpret_cast<const uint4*>(src);
+          const uint4 t = ld_stream(reinterpret_cast<const uint4*>(src));
           wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = t.z, wc[it][3] = t.w;
         } else {
-          const uint2 t = *reinterpret_cast<const uint2*>(src);
+          const uint2 t = ld_stream(reinterpret_cast<const uint2*>(src));
           wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = 0u, wc[it][3] = 0u;
         }
         vr[it] = vh[row];
@@ -247,7 +247,7 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       sn[t] = s;
       si[t] = inv;
       const int grow = base / G + lg;
-      if (grow * G < p.dv) hscales[(size_t)grow * DK + j] = s;
+      if (grow * G < p.dv) st_stream(hscales + (size_t)grow * DK + j, s);
     }
     __syncthreads();  // new scales in LDS
 
@@ -272,9 +272,9 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       if (row < p.dv) {
         uint8_t* dst = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
         if (lc.is8)
-          *reinterpret_cast<uint4*>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
+          st_stream(reinterpret_cast<uint4*>(dst), make_uint4(out[0], out[1], out[2], out[3]));
         else
-          *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+          st_stream(reinterpret_cast<uint2*>(dst), make_uint2(out[0], out[1]));
       }
     }
     __syncthreads();  // LDS free for the next block

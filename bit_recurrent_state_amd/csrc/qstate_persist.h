@@ -189,9 +189,9 @@ __device__ __forceinline__ void persist_class(const KParams& p, PState<MIXER, DK
     const float* hs = p.scales + head * p.dv * ngr;
     // 32-bit offsets from wave-uniform bases (a row is < 4096 rows of
     // <= 256 bytes into its head): scalar base + vector offset addressing
-    in.raw = *reinterpret_cast<const uint4*>(hc + (uint32_t)(row * Gm::ROW_BYTES + lr * 16));
-    in.s0 = hs[(uint32_t)(row * ngr + gcol)];
-    in.s1 = two_groups ? hs[(uint32_t)(row * ngr + gcol + 1)] : in.s0;
+    in.raw = ld_stream(reinterpret_cast<const uint4*>(hc + (uint32_t)(row * Gm::ROW_BYTES + lr * 16)));
+    in.s0 = ld_stream(hs + (uint32_t)(row * ngr + gcol));
+    in.s1 = two_groups ? ld_stream(hs + (uint32_t)(row * ngr + gcol + 1)) : in.s0;
     in.v = (p.v + head * p.dv)[(uint32_t)row];
     return in;
   };
@@ -263,12 +263,12 @@ __device__ __forceinline__ void persist_class(const KParams& p, PState<MIXER, DK
         const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
         const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
         if (store_ok) {
-          *reinterpret_cast<uint4*>(hcodes + (uint32_t)(row * Gm::ROW_BYTES + lr * 16)) = packed;
+          st_stream(reinterpret_cast<uint4*>(hcodes + (uint32_t)(row * Gm::ROW_BYTES + lr * 16)), packed);
           if constexpr (two_groups) {
-            hscales[(uint32_t)(row * ngr + gcol)] = s0;
-            hscales[(uint32_t)(row * ngr + gcol + 1)] = s1;
+            st_stream(hscales + (uint32_t)(row * ngr + gcol), s0);
+            st_stream(hscales + (uint32_t)(row * ngr + gcol + 1), s1);
           } else if (lr % LPG == 0) {
-            hscales[(uint32_t)(row * ngr + gcol)] = s0;
+            st_stream(hscales + (uint32_t)(row * ngr + gcol), s0);
           }
           if (oh && lr == 0) oh[row] = o;
         }

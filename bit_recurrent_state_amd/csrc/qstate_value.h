@@ -81,7 +81,7 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
   auto load = [&](int it) {
     RowIn in;
     const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
-    in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+    in.raw = ld_stream(reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16));
     in.s0 = hscales[(size_t)row * ngr + gcol];
     in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
     in.v = vh[row];
@@ -136,12 +136,12 @@ __device__ __forceinline__ void step_quant_head(const KParams& p, const Slice sl
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
       const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
       if (store_ok) {
-        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        st_stream(reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16), packed);
         if constexpr (two_groups) {
-          hscales[(size_t)row * ngr + gcol] = s0;
-          hscales[(size_t)row * ngr + gcol + 1] = s1;
+          st_stream(hscales + (size_t)row * ngr + gcol, s0);
+          st_stream(hscales + (size_t)row * ngr + gcol + 1, s1);
         } else if (lr % LPG == 0) {
-          hscales[(size_t)row * ngr + gcol] = s0;
+          st_stream(hscales + (size_t)row * ngr + gcol, s0);
         }
         if (oh && lr == 0) oh[row] = o;
       }
@@ -182,7 +182,7 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
   auto load = [&](int it) {
     FIn in;
     const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
-    loadv(hS + (size_t)row * DK + col0, in.x);
+    loadv_stream(hS + (size_t)row * DK + col0, in.x);
     in.v = vh[row];
     return in;
   };
@@ -217,7 +217,7 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
       ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
       const float o = row_sum<LPR>(lane_dot(d, qq));
       if (store_ok) {
-        storev(hS + (size_t)row * DK + col0, d);
+        storev_stream(hS + (size_t)row * DK + col0, d);
         if (oh && lr == 0) oh[row] = o;
       }
     }
@@ -327,6 +327,13 @@ __device__ __forceinline__ void store_block(uint8_t* dst, bool is8, const uint32
     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
 }
 
+__device__ __forceinline__ void store_block_stream(uint8_t* dst, bool is8, const uint32_t (&w)[4]) {
+  if (is8)
+    st_stream(reinterpret_cast<uint4*>(dst), make_uint4(w[0], w[1], w[2], w[3]));
+  else
+    st_stream(reinterpret_cast<uint2*>(dst), make_uint2(w[0], w[1]));
+}
+
 // Group absmax over the G/16 lanes of the lane's group, scale, and the
 // lane's 16 codes.
 template <int RND, int LPG>
@@ -382,8 +389,8 @@ __device__ __forceinline__ void step_mixed_head(const KParams& p, const Slice sl
     RowMixed in;
     const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
     const uint8_t* src = hcodes + (size_t)row * ml.row_bytes + ml.lane_off;
-    in.a = *reinterpret_cast<const uint2*>(src);
-    in.b = *reinterpret_cast<const uint2*>(src + half2);
+    in.a = ld_stream(reinterpret_cast<const uint2*>(src));
+    in.b = ld_stream(reinterpret_cast<const uint2*>(src + half2));
     in.s = hscales[(size_t)row * ngr + gcol];
     in.v = vh[row];
     return in;
@@ -432,8 +439,8 @@ __device__ __forceinline__ void step_mixed_head(const KParams& p, const Slice sl
       quantize_block<RND, LPG>(d, ml.is8, key, (uint32_t)((row * DK + col0) >> 4), w, s_old,
                                s_new, out);
       if (store_ok) {
-        store_block(hcodes + (size_t)row * ml.row_bytes + ml.lane_off, ml.is8, out);
-        if (lr % LPG == 0) hscales[(size_t)row * ngr + gcol] = s_new;
+        store_block_stream(hcodes + (size_t)row * ml.row_bytes + ml.lane_off, ml.is8, out);
+        if (lr % LPG == 0) st_stream(hscales + (size_t)row * ngr + gcol, s_new);
         if (oh && lr == 0) oh[row] = o;
       }
     }

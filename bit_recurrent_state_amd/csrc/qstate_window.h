@@ -284,7 +284,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   auto load = [&](int it) {
     RowW in;
     const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
-    in.raw = *reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16);
+    in.raw = ld_stream(reinterpret_cast<const uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16));
     in.a = load_arow<W>(wh.a + (size_t)row * W);
     in.s0 = hscales[(size_t)row * ngr + gcol];
     in.s1 = two_groups ? hscales[(size_t)row * ngr + gcol + 1] : in.s0;
@@ -404,12 +404,12 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
       const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
       if (store_ok) {
-        *reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16) = packed;
+        st_stream(reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16), packed);
         if constexpr (two_groups) {
-          hscales[(size_t)row * ngr + gcol] = s0;
-          hscales[(size_t)row * ngr + gcol + 1] = s1;
+          st_stream(hscales + (size_t)row * ngr + gcol, s0);
+          st_stream(hscales + (size_t)row * ngr + gcol + 1, s1);
         } else if (lr % LPG == 0) {
-          hscales[(size_t)row * ngr + gcol] = s0;
+          st_stream(hscales + (size_t)row * ngr + gcol, s0);
         }
         if (lr == 0) {
           if (oh) oh[row] = o;
