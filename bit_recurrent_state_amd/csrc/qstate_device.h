@@ -531,20 +531,20 @@ __device__ __forceinline__ void storev(float* ptr, const float (&x)[N]) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming accesses to the state.  A step reads every state byte once and
-// writes it once, from the same lane, and nothing touches it again before the
-// next step of the layer; the code (and FP32 state) loads and stores of the
-// step kernels therefore carry the non-temporal hint (`nt`), which keeps
-// these lines from displacing the reused ones (the heads' vectors) and lets
-// the written lines leave the caches early.  On the chip the hint is worth
-// 3-15 % of step time, but only on loads and stores together (either alone
-// changes nothing).  The hint changes cache policy only, not what a later
-// kernel reads.
+// Streaming accesses to the quantized state.  A step reads every code once
+// and writes it once, from the same lane, and nothing touches it again before
+// the next step of the layer; the code loads and stores of the quantized step
+// kernels (and the scale loads of the persistent one) therefore carry the
+// non-temporal hint (`nt`).  Measured on the chip: 3-15 % less step time,
+// but only with loads and stores together (either alone changes nothing);
+// the hint on the scale loads of the sliced kernel cost 3 %, and on the FP32
+// state step (four 16-byte loads per lane and row) it made the step 1.7x
+// slower, so those stay cached.  The hint changes cache policy only, not
+// what a later kernel reads.
 // ---------------------------------------------------------------------------
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -564,24 +564,6 @@ __device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
   __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(p));
 }
 __device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
-
-template <int N>
-__device__ __forceinline__ void loadv_stream(const float* ptr, float (&x)[N]) {
-#pragma unroll
-  for (int q = 0; q < N / 4; ++q) {
-    const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ptr) + q);
-    x[4 * q] = t[0], x[4 * q + 1] = t[1], x[4 * q + 2] = t[2], x[4 * q + 3] = t[3];
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void storev_stream(float* ptr, const float (&x)[N]) {
-#pragma unroll
-  for (int q = 0; q < N / 4; ++q) {
-    const f32x4_t t = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(ptr) + q);
-  }
-}
 
 // The wave's head and row slice [r0, r1).
 struct Slice {

@@ -182,7 +182,7 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
   auto load = [&](int it) {
     FIn in;
     const int row = min(sl.r0 + it * RPW + rsub, sl.r1 - 1);
-    loadv_stream(hS + (size_t)row * DK + col0, in.x);
+    loadv(hS + (size_t)row * DK + col0, in.x);
     in.v = vh[row];
     return in;
   };
@@ -217,7 +217,7 @@ __device__ __forceinline__ void step_fp32_head(const KParams& p, const Slice sl)
       ring[k] = load(it + kPrefetch);  // nothing of the slot is live any more
       const float o = row_sum<LPR>(lane_dot(d, qq));
       if (store_ok) {
-        storev_stream(hS + (size_t)row * DK + col0, d);
+        storev(hS + (size_t)row * DK + col0, d);
         if (oh && lr == 0) oh[row] = o;
       }
     }
