@@ -32,6 +32,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized-state decode steps/s and HBM GB/s (% of peak) at B=256, INT8/INT4"
 HBM_PEAK_GBPS = 8000.0
+# Vector ALU issue peak: 256 CUs x 4 SIMDs x 16 lanes per clock at 2.4 GHz
+# (a wave64 instruction issues over 4 clocks; no packed FP32 here), in
+# T lane-instructions/s.
+VALU_PEAK_TLANES = 256 * 4 * 16 * 2.4e9 / 1e12
 ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", f)
@@ -72,6 +76,21 @@ def measured_traffic(w):
     if not e or t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return e["hbm_bytes_per_launch"]
+
+
+def measured_valu(w):
+    """VALU wave-instructions per launch from the committed rocprofv3
+    SQ_INSTS_VALU count of this workload's step kernel; None when it was not
+    taken or the kernel source changed since."""
+    try:
+        import json as _j
+        t = _j.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(traffic_key(w))
+    if not e or t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return e.get("valu_wave_insts_per_launch")
 
 
 def gate_bytes(w) -> int:
@@ -365,6 +384,15 @@ def main():
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w),
                      "algorithmic_bytes_per_launch": nbytes},
     }
+    # The same launches against the vector-ALU issue rate (the INT4 + SR path
+    # is bound there): measured VALU instructions x 64 lanes / launch time.
+    vi = measured_valu(w)
+    if vi:
+        tl = vi * 64 / (ms * 1e-3) / 1e12
+        result["valu_roofline"] = {"bound": "alu", "achieved": tl, "peak": VALU_PEAK_TLANES,
+                                   "unit": "T lane-instructions/s", "frac": tl / VALU_PEAK_TLANES,
+                                   "wave_insts_per_launch": vi,
+                                   "lane_insts_per_state_element": vi * 64 / (w.B * w.H * w.dv * w.dk)}
 
     if not args.no_extras:
         result["accuracy_vs_fp32_state"] = fp32_accuracy(w, hb, Q, torch)
