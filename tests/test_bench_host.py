@@ -1,0 +1,112 @@
+"""Host-side checks of bench.py's measurement bookkeeping (no GPU needed):
+the algorithmic bytes of a step against figures counted by hand from the
+state layout, the per-kernel rocprofv3 records (HBM traffic, VALU
+instructions) tied to the kernel source they were taken on, and the
+one-GPU guard."""
+
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def Q():
+    from bit_recurrent_state_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from bit_recurrent_state_amd import qstate
+    return qstate
+
+
+def test_algorithmic_bytes_headline(Q):
+    """Gated DeltaNet, B=256, H=32, dk=dv=128, group 32: one head per batch row
+    (alpha_h > 0.99) is INT8, the other 31 are INT4.  Per head the codes
+    (dv*dk*n/8) and scales (dv*dk/G*4) are read and written once; q, k, v, o
+    are 4*(2*128 + 2*128) bytes; alpha and beta 4 bytes each."""
+    import bench
+    import workloads as W
+    w = W.WORKLOADS[2]
+    bb = bench.block_bits(w, Q)
+    assert sorted(set(bb.ravel().tolist())) == [4, 8]
+    assert int((bb[:, 0] == 8).sum()) == 1
+    int4_head = 2 * (128 * 128 // 2 + 128 * 4 * 4)  # 20480
+    int8_head = 2 * (128 * 128 + 128 * 4 * 4)       # 36864
+    io, gates = 4 * (2 * 128 + 2 * 128), 8
+    per_b = 31 * int4_head + int8_head + 32 * (io + gates)
+    assert bench.algorithmic_bytes(w, bb) == 256 * per_b == 188_809_216
+
+
+def test_algorithmic_bytes_gla(Q):
+    """GLA, B=256, H=16, dk=dv=128, INT8, group 64: alpha is one float per key
+    channel, no beta."""
+    import bench
+    import workloads as W
+    w = W.WORKLOADS[3]
+    bb = bench.block_bits(w, Q)
+    assert set(bb.ravel().tolist()) == {8}
+    head = 2 * (128 * 128 + 128 * 2 * 4) + 4 * (2 * 128 + 2 * 128) + 4 * 128
+    assert bench.algorithmic_bytes(w, bb) == 256 * 16 * head == 153_092_096
+
+
+def test_fp32_state_bytes():
+    import bench
+    import workloads as W
+    w = W.WORKLOADS[2]
+    head = 2 * 128 * 128 * 4 + 4 * (2 * 128 + 2 * 128) + 8
+    assert bench.fp32_bytes(w) == 256 * 32 * head
+
+
+def test_profile_records_follow_the_kernel_source(monkeypatch):
+    """The stored traffic and VALU counts are reported only while the kernel
+    source hash matches the one they were measured on."""
+    import bench
+    import workloads as W
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    w = W.WORKLOADS[2]
+    entry = rec["workloads"].get(bench.traffic_key(w))
+    assert entry is not None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["kernel_source_sha256_16"])
+    assert bench.measured_traffic(w) == entry["hbm_bytes_per_launch"]
+    assert bench.measured_valu(w) == entry.get("valu_wave_insts_per_launch")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.measured_traffic(w) is None
+    assert bench.measured_valu(w) is None
+
+
+def test_stored_records_are_calibrated():
+    """Each stored record scales FETCH_SIZE by 2 and WRITE_SIZE by 1, the
+    factors an in-place xor of known size gives on gfx950."""
+    import bench
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    assert len(rec["kernel_source_sha256_16"]) == 16
+    for key, e in rec["workloads"].items():
+        assert e["hbm_bytes_per_launch"] > 0, key
+        assert e["fetch_scale"] == pytest.approx(2.0, rel=1e-3), key
+        assert e["write_scale"] == pytest.approx(1.0, rel=1e-3), key
+
+
+def test_traffic_close_to_algorithmic_bytes(Q):
+    """Measured HBM bytes within 10 % above the algorithmic ones: every state
+    byte read once and written once, no re-reads."""
+    import bench
+    import workloads as W
+    rec = json.load(open(bench.TRAFFIC_FILE))["workloads"]
+    for wid in (2, 3):
+        w = W.WORKLOADS[wid]
+        e = rec[bench.traffic_key(w)]
+        alg = bench.algorithmic_bytes(w, bench.block_bits(w, Q))
+        assert 1.0 <= e["hbm_bytes_per_launch"] / alg < 1.10, (wid, e["hbm_bytes_per_launch"], alg)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
