@@ -39,7 +39,8 @@ VALU_PEAK_TLANES = 256 * 4 * 16 * 2.4e9 / 1e12
 ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", f)
-               for f in ("qstate_device.h", "qstate_value.h", "qstate_persist.h", "qstate_key.h")]
+               for f in ("qstate_device.h", "qstate_value.h", "qstate_persist.h", "qstate_key.h",
+                         "qstate_window.h")]
 
 
 def kernel_source_hash() -> str:
