@@ -67,6 +67,7 @@ def lib():
             "oracle_round_rtn": (i32, [f32, f32]),
             "oracle_round_sr": (i32, [f32, f32, u32, i32]),
             "oracle_round_bdr": (i32, [f32, f32, f32, f32, i32]),
+            "oracle_threshold_distance": (ctypes.c_double, [f32, f32, i32, u32, i32]),
             "oracle_codes_bytes": (ctypes.c_size_t, [cp, _P]),
             "oracle_head_offset": (ctypes.c_size_t, [cp, _P, i32, i32]),
             "oracle_get_code": (i32, [_P, i32, ctypes.c_int64]),
@@ -79,6 +80,9 @@ def lib():
             "oracle_head_readout": (None, [cp, _P, _P, _P, _P, _P]),
             "oracle_step": (None, [cp, _P, _P, _P, _P, _P, _P, _P, _P, _P, u64]),
             "oracle_step_fp32": (None, [cp, _P, _P, _P, _P, _P, _P, _P]),
+            "oracle_step_heads": (None, [cp, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, u64]),
+            "oracle_step_fp32_heads": (None, [cp, i32, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "oracle_quantize_heads": (None, [cp, _P, i32, _P, _P, _P, _P, u64]),
             "oracle_quantize": (None, [cp, _P, _P, _P, _P, u64]),
             "oracle_dequantize": (None, [cp, _P, _P, _P, _P]),
             "oracle_readout": (None, [cp, _P, _P, _P, _P, _P]),
@@ -196,6 +200,11 @@ def round_bdr(x: float, inv: float, s_new: float, prev: float, r: int) -> int:
     return lib().oracle_round_bdr(x, inv, s_new, prev, r)
 
 
+def threshold_distance(x: float, inv: float, stochastic: bool, r16: int, bits: int) -> float:
+    """Distance in code units from x*inv to the nearest point where the code changes."""
+    return lib().oracle_threshold_distance(x, inv, int(bool(stochastic)), r16, bits)
+
+
 def codes_bytes(c: Cfg, head_bits=None) -> int:
     hb = head_bits_array(c, head_bits)
     return lib().oracle_codes_bytes(ctypes.byref(c), _ptr(hb))
@@ -224,10 +233,10 @@ def unpack_head(c: Cfg, head_codes: np.ndarray, bits: int) -> np.ndarray:
 # ---- one head --------------------------------------------------------------
 
 def head_step(c: Cfg, b, h, bits, codes, scales, q, k, v, alpha, beta, step,
-              want_pre=False, want_xval=False):
+              want_pre=False, want_tdist=False):
     """One quantized step of one head; codes/scales (numpy) are updated in place.
 
-    Returns (o, pre, xval) with pre/xval None unless requested."""
+    Returns (o, pre, tdist) with pre/tdist None unless requested."""
     assert codes.dtype == np.uint8 and codes.flags.c_contiguous
     assert scales.dtype == np.float32 and scales.flags.c_contiguous
     bb = block_bits(c, bits)
@@ -238,11 +247,11 @@ def head_step(c: Cfg, b, h, bits, codes, scales, q, k, v, alpha, beta, step,
     assert alpha.size == (c.dk if c.mixer in (GLA, KDA) else 1)
     o = np.zeros(c.dv, np.float32)
     pre = np.zeros((c.dv, c.dk), np.float32) if want_pre else None
-    xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
+    tdist = np.zeros((c.dv, c.dk), np.float64) if want_tdist else None
     lib().oracle_head_step(ctypes.byref(c), b, h, _ptr(bb), _ptr(codes), _ptr(scales), _ptr(q),
                            _ptr(k), _ptr(v), _ptr(alpha), float(beta), _ptr(o), step,
-                           _ptr(pre), _ptr(xval))
-    return o, pre, xval
+                           _ptr(pre), _ptr(tdist))
+    return o, pre, tdist
 
 
 def head_step_fp32(c: Cfg, S, q, k, v, alpha, beta):
@@ -254,16 +263,16 @@ def head_step_fp32(c: Cfg, S, q, k, v, alpha, beta):
     return o
 
 
-def head_quantize(c: Cfg, b, h, bits, S, step, want_xval=False):
+def head_quantize(c: Cfg, b, h, bits, S, step, want_tdist=False):
     S = _f32(S)
     assert S.size == c.dv * c.dk
     bb = block_bits(c, bits)
     codes = np.zeros(head_code_bytes(c, bb), np.uint8)
     scales = np.zeros(int(np.prod(scales_shape(c))), np.float32)
-    xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
+    tdist = np.zeros((c.dv, c.dk), np.float64) if want_tdist else None
     lib().oracle_head_quantize(ctypes.byref(c), b, h, _ptr(bb), _ptr(S), _ptr(codes),
-                               _ptr(scales), step, _ptr(xval))
-    return codes, scales, xval
+                               _ptr(scales), step, _ptr(tdist))
+    return codes, scales, tdist
 
 
 def head_dequantize(c: Cfg, bits, codes, scales):
@@ -331,6 +340,41 @@ def readout(c: Cfg, head_bits, codes, scales, q):
     return o
 
 
+# ---- listed heads of a batch (thread-safe on disjoint lists) --------------------
+
+def _heads(heads):
+    return np.ascontiguousarray(np.asarray(heads, dtype=np.int32).reshape(-1))
+
+
+def step_heads(c: Cfg, head_bits, heads, codes, scales, q, k, v, alpha, beta, t, o=None):
+    """Quantized step of the listed heads (indices b*H + h) of full-batch arrays,
+    in place on codes/scales; o [B][H][dv] receives their readouts."""
+    hb = head_bits_array(c, head_bits)
+    idx = _heads(heads)
+    assert codes.dtype == np.uint8 and codes.flags.c_contiguous
+    assert scales.dtype == np.float32 and scales.flags.c_contiguous
+    for a in (q, k, v, alpha) + (() if beta is None else (beta,)):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    lib().oracle_step_heads(ctypes.byref(c), _ptr(hb), idx.size, _ptr(idx), _ptr(codes),
+                            _ptr(scales), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                            _ptr(o), t)
+
+
+def step_fp32_heads(c: Cfg, heads, S, q, k, v, alpha, beta, o=None):
+    idx = _heads(heads)
+    assert S.dtype == np.float32 and S.flags.c_contiguous
+    lib().oracle_step_fp32_heads(ctypes.byref(c), idx.size, _ptr(idx), _ptr(S), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o))
+
+
+def quantize_heads(c: Cfg, head_bits, heads, S, codes, scales, t):
+    hb = head_bits_array(c, head_bits)
+    idx = _heads(heads)
+    assert S.dtype == np.float32 and S.flags.c_contiguous
+    lib().oracle_quantize_heads(ctypes.byref(c), _ptr(hb), idx.size, _ptr(idx), _ptr(S),
+                                _ptr(codes), _ptr(scales), t)
+
+
 def bits_by_decay(retention, mode, thr_or_frac, lo=4, hi=8):
     ret = _f32(retention)
     out = np.zeros(ret.size, np.uint8)
@@ -355,7 +399,7 @@ def window_bytes(c: Cfg) -> int:
 
 
 def head_step_pw(c: Cfg, b, h, bits, codes, scales, window, q, k, v, alpha, beta, step,
-                 want_pre=False, want_xval=False):
+                 want_pre=False, want_tdist=False):
     """One quantized step of one head with its pure-write window (updated in place)."""
     bb = block_bits(c, bits)
     assert codes.size == head_code_bytes(c, bb) and window.size == window_bytes(c)
@@ -363,11 +407,11 @@ def head_step_pw(c: Cfg, b, h, bits, codes, scales, window, q, k, v, alpha, beta
     q, k, v, alpha = _f32(q), _f32(k), _f32(v), _f32(alpha)
     o = np.zeros(c.dv, np.float32)
     pre = np.zeros((c.dv, c.dk), np.float32) if want_pre else None
-    xval = np.zeros((c.dv, c.dk), np.float64) if want_xval else None
+    tdist = np.zeros((c.dv, c.dk), np.float64) if want_tdist else None
     lib().oracle_head_step_pw(ctypes.byref(c), b, h, _ptr(bb), _ptr(codes), _ptr(scales),
                               _ptr(window), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), float(beta),
-                              _ptr(o), step, _ptr(pre), _ptr(xval))
-    return o, pre, xval
+                              _ptr(o), step, _ptr(pre), _ptr(tdist))
+    return o, pre, tdist
 
 
 def head_window_state(c: Cfg, bits, codes, scales, window, step):

@@ -175,6 +175,38 @@ int oracle_round_bdr(float x, float inv, float s_new, float prev, int r) {
   return std::max(-r, std::min(r, n));
 }
 
+// Distance, in code units, from the pre-rounding value t = x*inv (exact) to
+// the nearest value of t at which the element's code changes, its random
+// bits held fixed.  Parity between two implementations of the quantizer
+// exempts a differing code only when this distance is tiny.
+//  * Round to nearest (and bounded directional rounding, which starts from
+//    it): the code steps from n to n + 1 at t = n + 1/2, for n in [-r, r-1].
+//  * Stochastic rounding with f fraction bits: the code is
+//    floor((N 2^(16-f) + r16) / 2^16) with N = RN(t 2^f), and N steps at the
+//    half-integers of t 2^f.  The code reaches n where N first satisfies
+//    N 2^(16-f) + r16 >= n 2^16.  For f = 16 that step sits at
+//    t = n - (r16 + 1/2) 2^-16; for f = 15 the first such N is
+//    ceil((n 2^16 - r16) / 2), and the step sits half a unit of 2^-15 below
+//    it: t = n - (r16 + 1) 2^-16 for even r16 and n - r16 2^-16 for odd r16,
+//    that is t = n - (r16 | 1) 2^-16.  So u = t + c 2^-16 (c = r16 + 1/2 or
+//    r16 | 1) crosses an integer n in [-r+1, r] exactly where the code
+//    steps from n - 1 to n (the clamp to [-r, r] removes the steps to r + 1
+//    and from -r - 1).
+// The double sums carry t's 48 significant bits; any rounding in them is
+// below 2^-50 code units.
+double oracle_threshold_distance(float x, float inv, int stochastic, uint32_t r16, int bits) {
+  const int r = qmax(bits);
+  const double t = (double)x * (double)inv;
+  if (!stochastic) {
+    const double h = std::max(-r + 0.5, std::min(r - 0.5, std::floor(t) + 0.5));
+    return std::fabs(t - h);
+  }
+  const double c = bits == 8 ? (double)((r16 & 0xFFFFu) | 1u) : (double)(r16 & 0xFFFFu) + 0.5;
+  const double u = t + c / 65536.0;
+  const double n = std::max((double)(-r + 1), std::min((double)r, std::nearbyint(u)));
+  return std::fabs(u - n);
+}
+
 // ---------------------------------------------------------------------------
 // Layout.  Bit widths are given per block of 16 key columns of a head
 // (LoReS 2/4: more bits for the slowest-decaying heads or channels; a head
@@ -299,7 +331,7 @@ static size_t scale_index(const oracle_cfg* c, int i, int j) {
 static void quantize_group(const oracle_cfg* c, const Layout& L, uint32_t key,
                            const std::vector<int64_t>& e, size_t si,
                            const float* S, const float* prev, uint8_t* codes,
-                           float* scales, double* xval) {
+                           float* scales, double* tdist) {
   const int bits = L.bits[(int)(e[0] % c->dk) / 16];
   const int r = qmax(bits);
   float m = 0.0f;
@@ -309,17 +341,16 @@ static void quantize_group(const oracle_cfg* c, const Layout& L, uint32_t key,
   scales[si] = s;
   for (int64_t x : e) {
     int n;
+    uint32_t r16 = 0;
     if (c->rounding == kRoundSR) {
-      const uint32_t r16 = oracle_sr_bits(key, (uint64_t)x);
+      r16 = oracle_sr_bits(key, (uint64_t)x);
       n = oracle_round_sr(S[x], inv, r16, bits);
-      if (xval) xval[x] = (double)S[x] * (double)inv + (double)r16 / 65536.0;
     } else if (c->rounding == kRoundBDR && prev) {
       n = oracle_round_bdr(S[x], inv, s, prev[x], r);
-      if (xval) xval[x] = (double)S[x] * (double)inv;
     } else {
       n = oracle_round_rtn(S[x], inv);
-      if (xval) xval[x] = (double)S[x] * (double)inv;
     }
+    if (tdist) tdist[x] = oracle_threshold_distance(S[x], inv, c->rounding == kRoundSR, r16, bits);
     n = std::max(-r, std::min(r, n));
     set_code_at(L, codes, (int)(x / c->dk), (int)(x % c->dk), n);
   }
@@ -327,20 +358,20 @@ static void quantize_group(const oracle_cfg* c, const Layout& L, uint32_t key,
 
 static void quantize_head(const oracle_cfg* c, const Layout& L, uint32_t key,
                           const float* S, const float* prev, uint8_t* codes,
-                          float* scales, double* xval) {
+                          float* scales, double* tdist) {
   const int dk = c->dk, dv = c->dv, G = c->G;
   std::vector<int64_t> e(G);
   if (c->axis == kAxisKey) {
     for (int g = 0; g < dv / G; ++g)
       for (int j = 0; j < dk; ++j) {
         for (int t = 0; t < G; ++t) e[t] = (int64_t)(g * G + t) * dk + j;
-        quantize_group(c, L, key, e, scale_index(c, g * G, j), S, prev, codes, scales, xval);
+        quantize_group(c, L, key, e, scale_index(c, g * G, j), S, prev, codes, scales, tdist);
       }
   } else {
     for (int i = 0; i < dv; ++i)
       for (int g = 0; g < dk / G; ++g) {
         for (int t = 0; t < G; ++t) e[t] = (int64_t)i * dk + g * G + t;
-        quantize_group(c, L, key, e, scale_index(c, i, g * G), S, prev, codes, scales, xval);
+        quantize_group(c, L, key, e, scale_index(c, i, g * G), S, prev, codes, scales, tdist);
       }
   }
 }
@@ -361,7 +392,7 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, const uint8_t* block_bi
                       uint8_t* codes, float* scales, const float* q,
                       const float* k, const float* v, const float* alpha,
                       float beta, float* o, uint64_t step, float* pre,
-                      double* xval) {
+                      double* tdist) {
   const int dk = c->dk, dv = c->dv;
   const Layout L = head_layout(c, block_bits);
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
@@ -394,7 +425,7 @@ void oracle_head_step(const oracle_cfg* c, int b, int h, const uint8_t* block_bi
     if (o) o[i] = oracle_dot(sp, q, dk);
   }
   if (pre) std::memcpy(pre, Sp.data(), sizeof(float) * Sp.size());
-  quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, xval);
+  quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, tdist);
 }
 
 // The same step on an unquantized FP32 state (the "FP32 states" the pages
@@ -424,9 +455,9 @@ void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
 
 void oracle_head_quantize(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                           const float* S, uint8_t* codes, float* scales,
-                          uint64_t step, double* xval) {
+                          uint64_t step, double* tdist) {
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
-  quantize_head(c, head_layout(c, block_bits), key, S, nullptr, codes, scales, xval);
+  quantize_head(c, head_layout(c, block_bits), key, S, nullptr, codes, scales, tdist);
 }
 
 void oracle_head_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
@@ -545,7 +576,7 @@ void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block
                          uint8_t* codes, float* scales, uint8_t* window,
                          const float* q, const float* k, const float* v,
                          const float* alpha, float beta, float* o, uint64_t step,
-                         float* pre, double* xval) {
+                         float* pre, double* tdist) {
   const int dk = c->dk, dv = c->dv, W = c->window;
   const Layout L = head_layout(c, block_bits);
   const uint32_t key = oracle_head_key(c->seed, c->layer, step, (uint32_t)b, (uint32_t)h);
@@ -619,7 +650,7 @@ void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block
     }
   }
   if (pre) std::memcpy(pre, Sp.data(), sizeof(float) * Sp.size());
-  quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, xval);
+  quantize_head(c, L, key, Sp.data(), stored.data(), codes, scales, tdist);
 
   // store the window: propagated keys of the remaining pairs (after a bypass
   // merge none remain), the new pair
@@ -750,6 +781,57 @@ void oracle_readout(const oracle_cfg* c, const uint8_t* block_bits, const uint8_
                           codes + oracle_head_offset(c, block_bits, b, h),
                           scales + bh * head_scales(c), q + bh * dk, o + bh * dv);
     }
+}
+
+// The same three operations on a list of heads (indices b*H + h) of a batch
+// in the library's layout; the other heads' data is neither read nor
+// written, so disjoint lists may run on separate threads.
+
+static size_t batch_head_offset(const oracle_cfg* c, const uint8_t* block_bits, int32_t bh) {
+  return oracle_head_offset(c, block_bits, bh / c->H, bh % c->H);
+}
+
+void oracle_step_heads(const oracle_cfg* c, const uint8_t* block_bits, int n,
+                       const int32_t* heads, uint8_t* codes, float* scales, const float* q,
+                       const float* k, const float* v, const float* alpha, const float* beta,
+                       float* o, uint64_t step) {
+  const int dk = c->dk, dv = c->dv;
+  const int na = vector_decay(c->mixer) ? dk : 1;
+  for (int t = 0; t < n; ++t) {
+    const size_t bh = (size_t)heads[t];
+    const int h = (int)(bh % c->H);
+    oracle_head_step(c, (int)(bh / c->H), h, block_bits + (size_t)h * (dk / 16),
+                     codes + batch_head_offset(c, block_bits, heads[t]),
+                     scales + bh * head_scales(c), q + bh * dk, k + bh * dk, v + bh * dv,
+                     alpha + bh * na, (c->mixer == kMixerGLA) ? 0.0f : beta[bh],
+                     o ? o + bh * dv : nullptr, step, nullptr, nullptr);
+  }
+}
+
+void oracle_step_fp32_heads(const oracle_cfg* c, int n, const int32_t* heads, float* S,
+                            const float* q, const float* k, const float* v,
+                            const float* alpha, const float* beta, float* o) {
+  const int dk = c->dk, dv = c->dv;
+  const int na = vector_decay(c->mixer) ? dk : 1;
+  for (int t = 0; t < n; ++t) {
+    const size_t bh = (size_t)heads[t];
+    oracle_head_step_fp32(c, S + bh * dv * dk, q + bh * dk, k + bh * dk, v + bh * dv,
+                          alpha + bh * na, (c->mixer == kMixerGLA) ? 0.0f : beta[bh],
+                          o ? o + bh * dv : nullptr);
+  }
+}
+
+void oracle_quantize_heads(const oracle_cfg* c, const uint8_t* block_bits, int n,
+                           const int32_t* heads, const float* S, uint8_t* codes,
+                           float* scales, uint64_t step) {
+  const int dk = c->dk, dv = c->dv;
+  for (int t = 0; t < n; ++t) {
+    const size_t bh = (size_t)heads[t];
+    const int h = (int)(bh % c->H);
+    oracle_head_quantize(c, (int)(bh / c->H), h, block_bits + (size_t)h * (dk / 16),
+                         S + bh * dv * dk, codes + batch_head_offset(c, block_bits, heads[t]),
+                         scales + bh * head_scales(c), step, nullptr);
+  }
 }
 
 // ---------------------------------------------------------------------------

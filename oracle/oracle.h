@@ -62,6 +62,9 @@ void oracle_group_scale(float m, int r, float* s, float* inv);
 int oracle_round_rtn(float x, float inv);
 int oracle_round_sr(float x, float inv, uint32_t r16, int bits);
 int oracle_round_bdr(float x, float inv, float s_new, float prev, int r);
+/* distance (code units) from x*inv to the nearest point where the code
+ * changes; stochastic != 0: stochastic rounding with the given r16 */
+double oracle_threshold_distance(float x, float inv, int stochastic, uint32_t r16, int bits);
 
 /* ---- layout ----
  * Bit widths come per block of 16 key columns: block_bits of one head holds
@@ -76,20 +79,21 @@ void oracle_set_code(uint8_t* head_codes, int bits, int64_t e, int code);
 /* ---- one head (b, h): buffers point at that head's data ---- */
 /* alpha: 1 value (GDN, scalar) or dk values (GLA, KDA); beta: beta (GDN,
  * KDA) / dt (scalar), unused for GLA.
- * o, pre, xval may be NULL.  pre receives S' [dv][dk] before requantizing;
- * xval receives the pre-rounding value per element (RTN: the exact product
- * S'*inv; SR: S'*inv + u, exact). */
+ * o, pre, tdist may be NULL.  pre receives S' [dv][dk] before requantizing;
+ * tdist receives, per element, the distance in code units from the exact
+ * pre-rounding value S'*inv to the nearest point where its code changes
+ * (oracle_threshold_distance). */
 void oracle_head_step(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                       uint8_t* codes, float* scales, const float* q,
                       const float* k, const float* v, const float* alpha,
                       float beta, float* o, uint64_t step, float* pre,
-                      double* xval);
+                      double* tdist);
 void oracle_head_step_fp32(const oracle_cfg* c, float* S, const float* q,
                            const float* k, const float* v, const float* alpha,
                            float beta, float* o);
 void oracle_head_quantize(const oracle_cfg* c, int b, int h, const uint8_t* block_bits,
                           const float* S, uint8_t* codes, float* scales,
-                          uint64_t step, double* xval);
+                          uint64_t step, double* tdist);
 void oracle_head_dequantize(const oracle_cfg* c, const uint8_t* block_bits,
                             const uint8_t* codes, const float* scales,
                             float* S);
@@ -113,6 +117,18 @@ void oracle_readout(const oracle_cfg* c, const uint8_t* block_bits,
                     const uint8_t* codes, const float* scales, const float* q,
                     float* o);
 
+/* the same on the listed heads only (indices b*H + h; other heads untouched) */
+void oracle_step_heads(const oracle_cfg* c, const uint8_t* block_bits, int n,
+                       const int32_t* heads, uint8_t* codes, float* scales, const float* q,
+                       const float* k, const float* v, const float* alpha, const float* beta,
+                       float* o, uint64_t step);
+void oracle_step_fp32_heads(const oracle_cfg* c, int n, const int32_t* heads, float* S,
+                            const float* q, const float* k, const float* v,
+                            const float* alpha, const float* beta, float* o);
+void oracle_quantize_heads(const oracle_cfg* c, const uint8_t* block_bits, int n,
+                           const int32_t* heads, const float* S, uint8_t* codes,
+                           float* scales, uint64_t step);
+
 /* ---- pure-write window: W FP8 (E4M3) pairs per head, see oracle.cpp ---- */
 float oracle_fp8_decode(uint8_t code);
 uint8_t oracle_fp8_encode(float x);
@@ -121,7 +137,7 @@ void oracle_head_step_pw(const oracle_cfg* c, int b, int h, const uint8_t* block
                          uint8_t* codes, float* scales, uint8_t* window,
                          const float* q, const float* k, const float* v,
                          const float* alpha, float beta, float* o, uint64_t step,
-                         float* pre, double* xval);
+                         float* pre, double* tdist);
 void oracle_head_window_state(const oracle_cfg* c, const uint8_t* block_bits,
                               const uint8_t* codes, const float* scales,
                               const uint8_t* window, uint64_t step, float* S);
