@@ -38,23 +38,13 @@ HBM_PEAK_GBPS = 8000.0
 VALU_PEAK_TLANES = 256 * 4 * 16 * 2.4e9 / 1e12
 ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRCS = [os.path.join(ROOT, "bit_recurrent_state_amd", "csrc", f)
-               for f in ("qstate_device.h", "qstate_value.h", "qstate_persist.h", "qstate_key.h",
-                         "qstate_window.h")]
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the decode kernels' code (all scale-group layouts), with
-    // comments and blank lines dropped so that comment edits keep it."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for f in KERNEL_SRCS:
-        for line in open(f).read().splitlines():
-            line = re.sub(r"//.*$", "", line).rstrip()
-            if line:
-                h.update(line.encode() + b"\n")
-    return h.hexdigest()[:16]
+    """The library's source hash (every source and header it is built from,
+    and the compile flags): stored profiler counts apply only to that build."""
+    from bit_recurrent_state_amd import build
+    return build.source_hash()
 
 
 def traffic_key(w) -> str:
@@ -178,10 +168,32 @@ def fp32_accuracy(w, hb, Q, torch, batch: int = 8, checkpoints=(1, 64, 256, 1024
             "note": "quantized vs FP32 state, same warm-up state and inputs"}
 
 
-def cpu_baseline(w, hb, seconds: float):
-    """The CPU reference on a sample of heads, one host thread per core (up to
-    16): heads are independent, so each thread steps its own heads; the
-    head-steps per second of all threads, scaled to steps/s of the workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, hb, seconds: float, single_seconds: float):
+    """The CPU reference on a sample of heads: one thread alone, then one
+    thread per host core (every core of the affinity mask).  Heads are
+    independent, so each thread steps its own heads; head-steps per second,
+    scaled to steps/s of the workload.  Each thread's heads (quantized state
+    and argument pointers) are prepared before the clock starts; the timed
+    loop only calls the reference's C entry point."""
+    import ctypes
     import threading
 
     import oracle
@@ -191,64 +203,256 @@ def cpu_baseline(w, hb, seconds: float):
     c = oracle.cfg(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, 0, 0, w.axis, w.window,
                    w.window_merge, w.lrb_threshold)
     q, k, v, alpha, beta = W.step_inputs(w, 0)
-    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096), rng.integers(0, w.H, 4096))]
     S0 = rng.standard_normal((w.dv, w.dk)).astype(np.float32)
-    try:
-        n_cpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n_cpu = os.cpu_count() or 1
-    workers = max(1, min(16, n_cpu))
-    counts = [0] * workers
+    L = oracle.lib()
+    P = ctypes.c_void_p
+    per_thread = 4
 
-    def run(wi, deadline):
-        # per head: its state and the argument pointers, prepared once; the
-        # timed loop only calls the reference's C entry point
-        import ctypes
-        L = oracle.lib()
-        P = ctypes.c_void_p
-        prepared = {}
-        n = 0
-        mine = heads[wi::workers]
-        while time.perf_counter() < deadline:
-            b, h = mine[n % len(mine)]
-            if (b, h) not in prepared:
+    def prepare(n_threads):
+        sets = []
+        for _ in range(n_threads):
+            mine = []
+            for b, h in zip(rng.integers(0, w.B, per_thread), rng.integers(0, w.H, per_thread)):
+                b, h = int(b), int(h)
                 codes, scales, _ = oracle.head_quantize(c, b, h, hb[h], S0, 0)
                 a = alpha[b, h] if w.mixer in (W.GLA, W.KDA) else np.float32([alpha[b, h]])
                 keep = [np.ascontiguousarray(x, np.float32) for x in (q[b, h], k[b, h], v[b, h], a)]
                 keep += [np.ascontiguousarray(hb[h], np.uint8), codes, scales,
                          np.zeros(max(oracle.window_bytes(c), 16), np.uint8)]
-                prepared[(b, h)] = (keep, [P(x.ctypes.data) for x in keep],
-                                    0.0 if beta is None else float(beta[b, h]))
-            keep, ptr, bt = prepared[(b, h)]
-            pq, pk, pv, pa, pbb, pc, ps, pw = ptr
-            if w.window:
-                L.oracle_head_step_pw(ctypes.byref(c), b, h, pbb, pc, ps, pw, pq, pk, pv, pa, bt,
-                                      None, 1 + n, None, None)
-            else:
-                L.oracle_head_step(ctypes.byref(c), b, h, pbb, pc, ps, pq, pk, pv, pa, bt, None,
-                                   1 + n, None, None)
-            n += 1
-        counts[wi] = n
+                mine.append((b, h, keep, [P(x.ctypes.data) for x in keep],
+                             0.0 if beta is None else float(beta[b, h])))
+            sets.append(mine)
+        return sets
 
-    oracle.lib()  # build/load once before the clock starts
-    t0 = time.perf_counter()
-    threads = [threading.Thread(target=run, args=(i, t0 + seconds)) for i in range(workers)]
-    for t in threads:
-        t.start()
-    for t in threads:
-        t.join()
-    dt = time.perf_counter() - t0
-    n = sum(counts)
+    def run(n_threads, secs):
+        sets = prepare(n_threads)
+        counts = [0] * n_threads
+        start = threading.Barrier(n_threads + 1)
+
+        def work(wi, deadline_box):
+            mine = sets[wi]
+            start.wait()
+            deadline = deadline_box[0]
+            n = 0
+            while time.perf_counter() < deadline:
+                b, h, _keep, ptr, bt = mine[n % len(mine)]
+                pq, pk, pv, pa, pbb, pc, ps, pw = ptr
+                if w.window:
+                    L.oracle_head_step_pw(ctypes.byref(c), b, h, pbb, pc, ps, pw, pq, pk, pv, pa,
+                                          bt, None, 1 + n, None, None)
+                else:
+                    L.oracle_head_step(ctypes.byref(c), b, h, pbb, pc, ps, pq, pk, pv, pa, bt,
+                                       None, 1 + n, None, None)
+                n += 1
+            counts[wi] = n
+
+        box = [0.0]
+        threads = [threading.Thread(target=work, args=(i, box)) for i in range(n_threads)]
+        for t in threads:
+            t.start()
+        box[0] = time.perf_counter() + secs
+        t0 = time.perf_counter()
+        start.wait()
+        for t in threads:
+            t.join()
+        dt = time.perf_counter() - t0
+        return sum(counts), dt
+
+    n1, dt1 = run(1, single_seconds)
+    cores = host_cores()
+    n, dt = run(cores, seconds)
+    heads = w.B * w.H
     return {
-        "value": n / dt / (w.B * w.H),
+        "value": n / dt / heads,
         "unit": "steps/s",
-        "cores": workers,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{n} head-steps of the same workload ({w.dv}x{w.dk} heads, "
-                  f"{ROUNDING_NAMES[w.rounding]}) in {dt:.1f} s on {workers} host threads "
-                  f"(one per core, disjoint heads; {dt * workers:.0f} CPU-seconds), scaled by "
-                  f"the {w.B * w.H} heads of one step",
+                  f"{ROUNDING_NAMES[w.rounding]}) in {dt:.1f} s on {cores} host threads "
+                  f"(every core of the affinity mask, disjoint heads; {dt * cores:.0f} "
+                  f"CPU-seconds), scaled by the {heads} heads of one step",
+        "single_thread": {"value": n1 / dt1 / heads, "unit": "steps/s", "cores": 1,
+                          "sample": f"{n1} head-steps in {dt1:.1f} s on one thread"},
+        "cpu_model": cpu_model(),
     }
+
+
+def input_pool(w, torch, first_t, min_bytes, layer=0):
+    """Pre-generated input batches (drawn on host threads, then copied to the
+    device) whose total size exceeds min_bytes, so that q, k, v and the gates
+    stream from HBM rather than from the 256 MB Infinity Cache."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads as W
+    one = W.step_inputs(w, first_t, 0, layer)
+    per = sum(x.nbytes for x in one if x is not None) + 4 * w.B * w.H * w.dv  # + o
+    n = max(2, int(np.ceil(min_bytes / per)))
+    with ThreadPoolExecutor(max_workers=min(16, host_cores())) as ex:
+        batches = list(ex.map(lambda t: W.step_inputs(w, t, 0, layer),
+                              range(first_t, first_t + n)))
+
+    def dev(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    pool = [tuple(map(dev, b)) for b in batches]
+    return pool, n * per
+
+
+def warm_state(w, Q, torch, layer=0):
+    """The workload's FP32 warm-up on the GPU from zero: the state every
+    instance is imported from."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads as W
+
+    def dev(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    f = Q.QState(Q.Config(w.B, w.H, w.dk, w.dv, 16, w.mixer, 0, True, None, 0, layer))
+    f.load_fp32(torch.zeros(w.B * w.H * w.dv * w.dk, device="cuda"))
+    with ThreadPoolExecutor(max_workers=min(16, host_cores())) as ex:
+        for inp in ex.map(lambda t: W.step_inputs(w, t, 0, layer), range(w.warmup)):
+            f.step(*map(dev, inp))
+    S = torch.empty(w.B * w.H * w.dv * w.dk, device="cuda")
+    f.store_fp32(S)
+    f.close()
+    return S
+
+
+def qconfig(Q, w, hb, layer):
+    uniform = bool(np.all(hb == hb[:, :1]))
+    return Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False,
+                    hb[:, 0].tolist() if uniform else None, 0, layer, w.axis,
+                    None if uniform else hb.tolist(), w.window, w.window_merge, w.lrb_threshold)
+
+
+def timed(torch, launches, steps, warm):
+    """ms per step: `launches` is a list of steps, each a list of (state,
+    inputs, o) launches; steps run round-robin over the list on torch's
+    current stream (the one the library launches on), timed with HIP events
+    on that stream."""
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        for st, inp, o in launches[i % len(launches)]:
+            st.step(*inp, o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        for st, inp, o in launches[i % len(launches)]:
+            st.step(*inp, o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def roofline(nbytes, ms):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": nbytes}
+
+
+def measure_workload(w, Q, torch, steps, warm, min_state_bytes=2**30, min_pool_bytes=320e6):
+    """Cold protocol for one single-layer workload: >= 1 GiB of independent
+    state instances (one per layer key), a > 320 MB input pool."""
+    hb = block_bits(w, Q)
+    cb, sb = Q.qstate_state_bytes(qconfig(Q, w, hb, 0))
+    n_states = max(2, int(np.ceil(min_state_bytes / (cb + sb))))
+    S = warm_state(w, Q, torch)
+    states = []
+    for layer in range(n_states):
+        st = Q.QState(qconfig(Q, w, hb, layer))
+        st.load_fp32(S)
+        states.append(st)
+    del S
+    pool, pool_bytes = input_pool(w, torch, w.warmup, min_pool_bytes)
+    o = torch.empty(w.B * w.H * w.dv, device="cuda")
+    launches = [[(states[i % n_states], pool[i % len(pool)], o)]
+                for i in range(n_states * len(pool))]
+    ms = timed(torch, launches, steps, warm)
+    nbytes = algorithmic_bytes(w, hb)
+    for st in states:
+        st.close()
+    del states, pool, launches
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "rounding": ROUNDING_NAMES[w.rounding], "B": w.B, "H": w.H,
+            "ms_per_step": ms, "steps_per_s": 1e3 / ms, "roofline": roofline(nbytes, ms),
+            "state_instances": n_states, "state_MB_each": round((cb + sb) / 1e6, 1),
+            "input_pool_MB": round(pool_bytes / 1e6, 1), "steps": steps}
+
+
+def measure_layer_stack(w, Q, torch, steps, warm, min_pool_bytes=320e6):
+    """The Mamba2-style stack as one step: w.layers independent states (layer
+    keys 0..L-1, widths by each layer's decay ranking), one launch each per
+    step.  Every layer is imported from the same FP32 warm-up (layer 0's
+    inputs); the input pool is shared by the layers."""
+    import workloads as W
+    S = warm_state(w, Q, torch)
+    states, nbytes, sbytes = [], 0, 0
+    for layer in range(w.layers):
+        rule = {"rank_half": (1, 0.5), "alpha_gt_0.99": (0, 0.99)}[w.bits_policy]
+        hb1 = Q.qstate_bits_by_decay(W.head_retention(w, 0, layer), *rule)
+        hb = np.repeat(hb1[:, None], w.dk // 16, axis=1).astype(np.uint8)
+        st = Q.QState(qconfig(Q, w, hb, layer))
+        st.load_fp32(S)
+        states.append(st)
+        nbytes += algorithmic_bytes(w, hb)
+        cb, sb = Q.qstate_state_bytes(qconfig(Q, w, hb, layer))
+        sbytes += cb + sb
+    del S
+    pool, pool_bytes = input_pool(w, torch, w.warmup, min_pool_bytes)
+    o = torch.empty(w.B * w.H * w.dv, device="cuda")
+    launches = [[(states[l], pool[(i * w.layers + l) % len(pool)], o) for l in range(w.layers)]
+                for i in range(len(pool))]
+    ms = timed(torch, launches, steps, warm)
+    for st in states:
+        st.close()
+    del states, pool, launches
+    torch.cuda.empty_cache()
+    rf = roofline(nbytes, ms)
+    return {"workload": w.name, "rounding": ROUNDING_NAMES[w.rounding], "B": w.B, "H": w.H,
+            "layers": w.layers, "ms_per_step": ms, "steps_per_s": 1e3 / ms,
+            "ms_per_layer_launch": ms / w.layers, "roofline": rf,
+            "state_MB_all_layers": round(sbytes / 1e6, 1),
+            "input_pool_MB": round(pool_bytes / 1e6, 1), "steps": steps,
+            "note": "one step = one launch per layer; layers imported from one FP32 warm-up"}
+
+
+def ceilings(Q, torch, nbytes=2**31, reps=20):
+    """The library's own bandwidth-ceiling kernels on a 2 GiB buffer (8x the
+    Infinity Cache): streaming copy and in-place read-modify-write, with and
+    without the non-temporal hint; GB/s counts bytes read plus written."""
+    import ctypes
+
+    from bit_recurrent_state_amd._lib import check, lib
+    L = lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    out = {}
+    for name, fn in (("copy", lambda nt: L.qstate_ceiling_copy(ctypes.c_void_p(a.data_ptr()),
+                                                             ctypes.c_void_p(b.data_ptr()),
+                                                             nbytes, nt, sp)),
+                     ("rmw", lambda nt: L.qstate_ceiling_rmw(ctypes.c_void_p(a.data_ptr()),
+                                                           nbytes, 0x5A5A5A5A, nt, sp))):
+        for nt in (1, 0):
+            for _ in range(3):
+                check(f"qstate_ceiling_{name}", fn(nt))
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn(nt)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[f"{name}{'_nt' if nt else ''}_gbps"] = 2 * nbytes / (ms * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    out["kernel"] = "qstate_ceiling_copy / qstate_ceiling_rmw, 2 GiB, 16 B per lane access"
+    return out
 
 
 def main():
@@ -268,10 +472,14 @@ def main():
     ap.add_argument("--bits", choices=["int4", "int8"], default=None,
                     help="override the per-head width policy: every head INT4 or INT8")
     ap.add_argument("--states", type=int, default=0, help="state instances (0: >= 1 GiB)")
-    ap.add_argument("--pool", type=int, default=16, help="pre-generated input batches")
-    ap.add_argument("--cpu-seconds", type=float, default=1.5,
-                    help="wall seconds of the CPU-reference sample (on every host core)")
-    ap.add_argument("--no-extras", action="store_true", help="skip hot/fp32/copy figures")
+    ap.add_argument("--pool-mb", type=float, default=320.0,
+                    help="pre-generated input batches of at least this many MB")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="wall seconds of the CPU-reference sample on every host core")
+    ap.add_argument("--cpu-single-seconds", type=float, default=4.0,
+                    help="wall seconds of the single-thread CPU-reference sample")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads, hot, FP32-state and ceiling figures")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -305,55 +513,25 @@ def main():
     uniform = bool(np.all(hb == hb[:, :1]))
     nbytes = algorithmic_bytes(w, hb)
 
-    def qcfg(layer):
-        return Q.Config(w.B, w.H, w.dk, w.dv, w.G, w.mixer, w.rounding, False,
-                        hb[:, 0].tolist() if uniform else None, 0, layer, w.axis,
-                        None if uniform else hb.tolist(), w.window, w.window_merge,
-                        w.lrb_threshold)
-
-    cfg0 = qcfg(0)
-    cb, sb = Q.qstate_state_bytes(cfg0)
+    cb, sb = Q.qstate_state_bytes(qconfig(Q, w, hb, 0))
     n_states = args.states or max(2, int(np.ceil(1.0 * 2**30 / (cb + sb))))
-
-    # initial state: FP32 warm-up on the GPU from zero, then the import
-    fcfg = Q.Config(w.B, w.H, w.dk, w.dv, 16, w.mixer, 0, True, None, 0, 0)
-    f = Q.QState(fcfg)
-    f.load_fp32(torch.zeros(w.B * w.H * w.dv * w.dk, device="cuda"))
-
-    def dev(x):
-        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
-
-    for t in range(w.warmup):
-        f.step(*map(dev, W.step_inputs(w, t)))
-    S = torch.empty(w.B * w.H * w.dv * w.dk, device="cuda")
-    f.store_fp32(S)
-    f.close()
+    S = warm_state(w, Q, torch)
     states = []
     for layer in range(n_states):
-        s = Q.QState(qcfg(layer))
-        s.load_fp32(S)
-        states.append(s)
+        st = Q.QState(qconfig(Q, w, hb, layer))
+        st.load_fp32(S)
+        states.append(st)
     del S
-    pool = [tuple(map(dev, W.step_inputs(w, w.warmup + i))) for i in range(args.pool)]
+    pool, pool_bytes = input_pool(w, torch, w.warmup, args.pool_mb * 1e6)
     o = torch.empty(w.B * w.H * w.dv, device="cuda")
     torch.cuda.synchronize()
+    launches = [[(states[i % n_states], pool[i % len(pool)], o)]
+                for i in range(n_states * len(pool))]
 
-    stream = torch.cuda.current_stream()
-
-    def timed(run_states, steps, warm):
-        for i in range(warm):
-            run_states[i % len(run_states)].step(*pool[i % len(pool)], o)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            run_states[i % len(run_states)].step(*pool[i % len(pool)], o)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps  # ms per step
-
-    ms = timed(states, args.steps, args.warmup)
-    gbps = nbytes / (ms * 1e-3) / 1e9
+    ms = timed(torch, launches, args.steps, args.warmup)
+    rf = roofline(nbytes, ms)
+    rf["traffic"] = measured_traffic(w)
+    gbps = rf["achieved"]
     result = {
         "metric": METRIC,
         "value": 1e3 / ms,
@@ -377,13 +555,12 @@ def main():
             "group_axis": "key" if w.axis else "value", "window": w.window,
             **({"low_rank_bypass_threshold": w.lrb_threshold} if w.window_merge else {}),
             "state_instances": n_states,
-            "state_MB_each": round((cb + sb) / 1e6, 1), "input_pool": args.pool,
+            "state_MB_each": round((cb + sb) / 1e6, 1),
+            "input_pool_MB": round(pool_bytes / 1e6, 1), "input_batches": len(pool),
         },
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w),
-                     "algorithmic_bytes_per_launch": nbytes},
+        "roofline": rf,
     }
     # The same launches against the vector-ALU issue rate (the INT4 + SR path
     # is bound there): measured VALU instructions x 64 lanes / launch time.
@@ -397,13 +574,27 @@ def main():
 
     if not args.no_extras:
         result["accuracy_vs_fp32_state"] = fp32_accuracy(w, hb, Q, torch)
-        ms_hot = timed(states[:1], args.steps, args.warmup)
+        ms_hot = timed(torch, [[(states[0], pool[i % len(pool)], o)] for i in range(len(pool))],
+                       args.steps, args.warmup)
         result["hot_single_state"] = {"ms_per_step": ms_hot, "steps_per_s": 1e3 / ms_hot,
                                       "effective_gbps": nbytes / (ms_hot * 1e-3) / 1e9}
-        for s in states:
-            s.close()
-        states.clear()
-        torch.cuda.empty_cache()
+    for st in states:
+        st.close()
+    del states, pool, launches
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        steps_x = max(args.steps, 200)
+        # the other B = 256 workload (GLA, INT8, group 64), both roundings, and
+        # the 24-layer Mamba2-style stack as one step
+        others = {}
+        for rnd in (W.RTN, W.SR):
+            wx = W.WORKLOADS[3].scaled(rounding=rnd)
+            others[f"{wx.name}_{ROUNDING_NAMES[rnd].lower()}"] = measure_workload(
+                wx, Q, torch, steps_x, 20)
+        w4 = W.WORKLOADS[4]
+        others[w4.name] = measure_layer_stack(w4, Q, torch, max(20, steps_x // 10), 3)
+        result["other_workloads"] = others
         # FP32-state baseline kernel, same protocol
         fb = fp32_bytes(w)
         n_f = max(2, int(np.ceil(1.0 * 2**30 / (fb / 2))))
@@ -412,46 +603,23 @@ def main():
             fs = Q.QState(Q.Config(w.B, w.H, w.dk, w.dv, 16, w.mixer, 0, True, None, 0, layer))
             fs.load_fp32(torch.zeros(w.B * w.H * w.dv * w.dk, device="cuda"))
             fstates.append(fs)
-        ms_f = timed(fstates, max(200, args.steps // 4), 10)
+        fpool, _ = input_pool(w, torch, w.warmup, 0)
+        of = torch.empty(w.B * w.H * w.dv, device="cuda")
+        ms_f = timed(torch, [[(fstates[i % n_f], fpool[i % len(fpool)], of)]
+                             for i in range(n_f * len(fpool))], max(200, args.steps // 4), 10)
         result["fp32_state_baseline"] = {
             "ms_per_step": ms_f, "steps_per_s": 1e3 / ms_f, "state_instances": n_f,
             "gbps": fb / (ms_f * 1e-3) / 1e9, "speedup_of_quantized": ms_f / ms}
         for fs in fstates:
             fs.close()
-        fstates.clear()
+        del fstates, fpool
         torch.cuda.empty_cache()
-        # plain device copy (read + write) as the box's achievable ceiling
-        n = 1 << 29
-        a = torch.empty(n, dtype=torch.float32, device="cuda")
-        bb = torch.empty_like(a)
-        for _ in range(3):
-            bb.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(20):
-            bb.copy_(a)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        result["copy_ceiling_gbps"] = 2 * 4 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del bb
-        # plain in-place read-modify-write of the same size (the state update's access pattern)
-        ai = a.view(torch.int32)
-        for _ in range(3):
-            ai.bitwise_xor_(0x5A5A5A5A)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(20):
-            ai.bitwise_xor_(0x5A5A5A5A)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        result["rmw_ceiling_gbps"] = 2 * 4 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        result["hbm_frac_of_rmw_ceiling"] = gbps / result["rmw_ceiling_gbps"]
-        del a, ai
-        torch.cuda.empty_cache()
+        cl = ceilings(Q, torch)
+        result["ceiling"] = cl
+        result["hbm_frac_of_rmw_ceiling"] = gbps / max(cl["rmw_nt_gbps"], cl["rmw_gbps"])
 
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, hb, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, hb, args.cpu_seconds, args.cpu_single_seconds)
     print(json.dumps(result), flush=True)
 
 

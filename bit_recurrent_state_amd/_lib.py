@@ -27,6 +27,8 @@ EXPORTS = (
     "qstate_readout", "qstate_store_fp32", "qstate_get_step", "qstate_set_step",
     "qstate_destroy", "qstate_strerror", "qstate_bits_by_decay",
 )
+# include/qstate_ceiling.h: bandwidth-ceiling kernels (measurement support)
+CEILING_EXPORTS = ("qstate_ceiling_copy", "qstate_ceiling_rmw")
 
 
 class QStateConfig(ctypes.Structure):
@@ -51,6 +53,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run "
                           "python -m bit_recurrent_state_amd.build")
+    from . import build
+    if all(os.path.exists(f) for f in build.SOURCES + build.HEADERS) and build.stale():
+        raise ImportError(f"{LIB_PATH} was built from other sources or flags than those in "
+                          "the package: run python -m bit_recurrent_state_amd.build")
     L = ctypes.CDLL(LIB_PATH)
     P, c_int, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     cfgp = ctypes.POINTER(QStateConfig)
@@ -67,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "qstate_strerror": (ctypes.c_char_p, [c_int]),
         "qstate_bits_by_decay": (c_int, [P, c_int, c_int, ctypes.c_float, ctypes.c_uint8,
                                          ctypes.c_uint8, P]),
+        "qstate_ceiling_copy": (c_int, [P, P, sz, c_int, P]),
+        "qstate_ceiling_rmw": (c_int, [P, sz, ctypes.c_uint32, c_int, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)

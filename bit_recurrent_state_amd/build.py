@@ -21,8 +21,9 @@ SOURCES = ([os.path.join(CSRC, f"qstate_window_dk{dk}_w{w}.hip")
             for dk in (64, 128, 256) for w in (4, 8, 16)]
            + [os.path.join(CSRC, f"qstate_{kind}_dk{dk}.hip")
               for kind in ("value", "key") for dk in (64, 128, 256)]
+           + [os.path.join(CSRC, "qstate_ceiling.hip")]
            + [os.path.join(CSRC, "qstate_dispatch.cpp"), os.path.join(CSRC, "qstate_api.cpp")])
-HEADERS = [os.path.join(ROOT, "include", "qstate.h")] + [
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("qstate.h", "qstate_ceiling.h")] + [
     os.path.join(CSRC, h) for h in ("qstate_launch.h", "qstate_device.h", "qstate_value.h",
                                     "qstate_key.h", "qstate_window.h",
                                     "qstate_persist.h")]
@@ -59,18 +60,40 @@ def build(out: str = LIB, extra=(), jobs: int = 0) -> str:
             failed.append(src)
     if failed:
         raise subprocess.CalledProcessError(1, f"hipcc: {', '.join(failed)}")
+    digest = source_hash()
     tmp = out + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                    check=True)
     os.replace(tmp, out)
+    if out == LIB:
+        with open(HASH_FILE, "w") as fh:
+            fh.write(digest + "\n")
     return out
 
 
+HASH_FILE = LIB + ".srchash"
+
+
+def source_hash() -> str:
+    """sha256[:16] of every source and header the library is built from and
+    of the compile flags: a built library records it, and a library whose
+    record differs from the sources at hand is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(SOURCES + HEADERS):
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update("\0".join(FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
 def stale() -> bool:
-    if not os.path.exists(LIB):
+    """True when the library is missing or was built from other sources or flags."""
+    if not os.path.exists(LIB) or not os.path.exists(HASH_FILE):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(f) > t for f in SOURCES + HEADERS)
+    with open(HASH_FILE) as fh:
+        return fh.read().strip() != source_hash()
 
 
 if __name__ == "__main__":

@@ -18,6 +18,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.cpp")
 LIB = os.path.join(HERE, "liboracle.so")
+# A separately built copy (e.g. the sanitizer build of tests/test_sanitizers.py)
+# may be loaded instead by naming it in QSTATE_ORACLE_LIB.
+LIB_OVERRIDE = os.environ.get("QSTATE_ORACLE_LIB")
 
 GDN, GLA, SCALAR, KDA = 0, 1, 2, 3
 RTN, SR, BDR = 0, 1, 2
@@ -53,7 +56,7 @@ _P = ctypes.c_void_p
 def lib():
     global _lib
     if _lib is None:
-        L = ctypes.CDLL(build())
+        L = ctypes.CDLL(LIB_OVERRIDE if LIB_OVERRIDE else build())
         u64, u32, i32, f32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_float
         cp = ctypes.POINTER(Cfg)
         sig = {

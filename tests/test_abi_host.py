@@ -21,8 +21,8 @@ def L():
     return lib()
 
 
-def _header_functions():
-    text = open(os.path.join(ROOT, "include", "qstate.h")).read()
+def _header_functions(header="qstate.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(qstate_\w+)\s*\(", text, re.M)))
 
@@ -30,10 +30,29 @@ def _header_functions():
 def test_exports_every_declared_symbol(L):
     names = _header_functions()
     assert len(names) >= 11
-    from bit_recurrent_state_amd._lib import EXPORTS
+    from bit_recurrent_state_amd._lib import CEILING_EXPORTS, EXPORTS
     assert sorted(EXPORTS) == names
-    for n in names:
+    ceiling = _header_functions("qstate_ceiling.h")
+    assert sorted(CEILING_EXPORTS) == ceiling and len(ceiling) == 2
+    for n in names + ceiling:
         assert hasattr(L, n), n
+
+
+def test_ceiling_kernels_check_arguments(L):
+    """Null, misaligned, odd-sized, overlapping or bad-flag calls are refused
+    before any launch."""
+    P = ctypes.c_void_p
+    a, b = P(4096), P(4096 + (1 << 20))
+    assert L.qstate_ceiling_copy(None, b, 1024, 1, None) == -1
+    assert L.qstate_ceiling_copy(a, P(4096 + 8), 1024, 1, None) == -1
+    assert L.qstate_ceiling_copy(a, b, 1000, 1, None) == -1
+    assert L.qstate_ceiling_copy(a, b, 1024, 2, None) == -1
+    assert L.qstate_ceiling_copy(a, P(4096 + 512), 1024, 0, None) == -1  # overlap
+    assert L.qstate_ceiling_copy(a, b, 0, 1, None) == 0  # nothing to move
+    assert L.qstate_ceiling_rmw(None, 1024, 1, 1, None) == -1
+    assert L.qstate_ceiling_rmw(P(4100), 1024, 1, 1, None) == -1
+    assert L.qstate_ceiling_rmw(a, 24, 1, 0, None) == -1
+    assert L.qstate_ceiling_rmw(a, 0, 1, 0, None) == 0
 
 
 def _cfg(**kw):

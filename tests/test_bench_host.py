@@ -9,6 +9,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -109,3 +110,38 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_algorithmic_bytes_layer_stack(Q):
+    """Mamba2-style stack: 24 layers, each B=512, H=32, dv=64 (head dim),
+    dk=128 (state dim), group 64, half the heads INT8 (slowest decay of that
+    layer) and half INT4; scalar decay: one alpha and one dt per head."""
+    import bench
+    import workloads as W
+    w = W.WORKLOADS[4]
+    assert w.layers == 24
+    int8_head = 2 * (64 * 128 + 64 * 2 * 4)
+    int4_head = 2 * (64 * 128 // 2 + 64 * 2 * 4)
+    io, gates = 4 * (2 * 128 + 2 * 64), 8
+    per_layer = 512 * (16 * int8_head + 16 * int4_head + 32 * (io + gates))
+    for layer in (0, 7, 23):
+        hb1 = Q.qstate_bits_by_decay(W.head_retention(w, 0, layer), 1, 0.5)
+        assert int((hb1 == 8).sum()) == 16
+        hb = np.repeat(hb1[:, None], w.dk // 16, axis=1).astype(np.uint8)
+        assert bench.algorithmic_bytes(w, hb) == per_layer
+    assert 24 * per_layer == 5_841_616_896
+
+
+def test_cpu_baseline_reports_every_core_and_one(monkeypatch):
+    """The reference timed on one thread and on every core of the affinity
+    mask, with the CPU model; the sample runs briefly here."""
+    import bench
+    import workloads as W
+    w = W.WORKLOADS[2]
+    hb = np.repeat(np.array([4] * 31 + [8], np.uint8)[:, None], 8, axis=1)
+    r = bench.cpu_baseline(w, hb, 0.3, 0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "steps/s"
+    assert r["cores"] == bench.host_cores() >= 1
+    assert r["single_thread"]["cores"] == 1
+    assert r["value"] > 0 and r["single_thread"]["value"] > 0
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
