@@ -32,10 +32,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized-state decode steps/s and HBM GB/s (% of peak) at B=256, INT8/INT4"
 HBM_PEAK_GBPS = 8000.0
-# Vector ALU issue peak: 256 CUs x 4 SIMDs x 16 lanes per clock at 2.4 GHz
-# (a wave64 instruction issues over 4 clocks; no packed FP32 here), in
-# T lane-instructions/s.
-VALU_PEAK_TLANES = 256 * 4 * 16 * 2.4e9 / 1e12
+# Vector ALU issue peak, in T lane-instructions/s: the published FP32 vector
+# rate (157.3 TFLOP/s = 256 CUs x 4 SIMDs x 32 FMA lanes per clock x 2 flops
+# at 2.4 GHz), i.e. one wave64 FP32 instruction per SIMD every 2 clocks.
+# Integer, conversion, SDWA/DPP and three-operand min/max forms take longer
+# per instruction, so a real mix stays below this figure even when issue-bound.
+VALU_PEAK_TLANES = 256 * 4 * 32 * 2.4e9 / 1e12
 ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -480,6 +482,9 @@ def main():
                     help="wall seconds of the single-thread CPU-reference sample")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads, hot, FP32-state and ceiling figures")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the ceiling kernels even with --no-extras (their known "
+                         "byte counts calibrate profiler traffic counters in the same run)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -614,6 +619,7 @@ def main():
             fs.close()
         del fstates, fpool
         torch.cuda.empty_cache()
+    if not args.no_extras or args.ceilings:
         cl = ceilings(Q, torch)
         result["ceiling"] = cl
         result["hbm_frac_of_rmw_ceiling"] = gbps / max(cl["rmw_nt_gbps"], cl["rmw_gbps"])

@@ -305,6 +305,39 @@ __device__ __forceinline__ uint32_t sr_word(float y, uint32_t r16) {
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
+// Bounded directional rounding of one element.  y = kMagic + n holds the
+// nearest code n of the updated value x, pv the value stored before the step,
+// s_new the new scale, r the code range.  Where pv lies strictly between
+// n*s_new and x, step one code toward x; then clamp to [-r, r].  (y stays in
+// the magic's binade, so +-1 is exact.)
+__device__ __forceinline__ float bdr_adjust(float y, float x, float pv, float s_new, float r) {
+  const float st = (y - kMagic) * s_new;
+  if (x > pv && st < pv) y += 1.0f;
+  if (x < pv && st > pv) y -= 1.0f;
+  return fminf(fmaxf(y, kMagic - r), kMagic + r);
+}
+
+// The same decision without compares, on the bit pattern of y, for the INT4
+// lanes of the value-axis step (measured faster there than the compares,
+// which the INT8 and key-axis paths keep).  With a = pv - x and
+// b = n*s_new - pv (signs exact), pv lies strictly between n*s_new and x
+// exactly when a and b are nonzero with one sign, the sign opposite to the
+// step; med3(a, b, 0) is then the one of them nearer zero, and zero
+// otherwise.  Neither a nor b can be -0: pv = c*s_old - 2^(n-1)*s_old is zero
+// only by exact cancellation, which rounds to +0, and n*s_new is -0 only for
+// n < 0 with s_new = 0, while a zero scale has every n = 0.  So the bit
+// pattern of med3's result, read as an integer and clamped to [-1, 1], is
+// minus the step, and the codes, bit patterns of floats of one binade, order
+// as integers for the final clamp.
+__device__ __forceinline__ uint32_t bdr_adjust_bits(uint32_t ybits, float x, float pv, float s_new,
+                                                    float r) {
+  const float st = (__uint_as_float(ybits) - kMagic) * s_new;
+  const float m = __builtin_amdgcn_fmed3f(pv - x, st - pv, 0.0f);
+  const int t = min(max(__float_as_int(m), -1), 1);
+  const int lo = __float_as_int(kMagic - r), hi = __float_as_int(kMagic + r);
+  return (uint32_t)min(max((int)ybits - t, lo), hi);
+}
+
 // Requantize one 16-element chunk with inverse scale inv into 16 packed codes
 // (four words for INT8, two for INT4).  block: the chunk's 16-element block
 // index in the head (stochastic rounding).  wprev / s_old: the chunk's codes
@@ -336,25 +369,29 @@ __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t 
 #pragma unroll
     for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv, kMagic));
     if constexpr (RND == kBDR) {
-      // prev = c*s_old exactly as stored; the nearest code's stored value
-      // (y - magic)*s_new; where prev lies strictly between that value and
-      // S', step one code toward S' (y stays in the magic's binade, so +-1
-      // is exact), then clamp to [-r, r].
-      constexpr int R = (1 << (BITS - 1)) - 1;
-      constexpr float bias = (float)(1 << (BITS - 1));
-      float prev[16];
-      unpack16<BITS>(wprev, prev);
-      const float nb = -bias * s_old;
+      // prev = c*s_old exactly as stored
+      constexpr float R = (float)((1 << (BITS - 1)) - 1);
+      if constexpr (BITS == 4) {
+        // widened as the step's dequantization widens INT4 codes; the words
+        // pass through an empty asm so that the widening is redone here
+        // rather than kept live from the dequantization (E more registers
+        // through the whole update)
+        uint32_t wp[2] = {wprev[0], wprev[1]};
+        asm("" : "+v"(wp[0]));
+        asm("" : "+v"(wp[1]));
+        float pv[16];
+        dequant_lane<4, 16>(wp, s_old, s_old, pv);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pv = __builtin_fmaf(prev[j], s_old, nb);
-        float y = __uint_as_float(src[j]);
-        const float st = (y - kMagic) * s_new;
-        const float x = sp[j];
-        if (x > pv && st < pv) y += 1.0f;
-        if (x < pv && st > pv) y -= 1.0f;
-        y = fminf(fmaxf(y, kMagic - (float)R), kMagic + (float)R);
-        src[j] = __float_as_uint(y);
+        for (int j = 0; j < 16; ++j) src[j] = bdr_adjust_bits(src[j], sp[j], pv[j], s_new, R);
+      } else {
+        float prev[16];
+        unpack16<BITS>(wprev, prev);
+        const float nb = -128.0f * s_old;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float pv = __builtin_fmaf(prev[j], s_old, nb);
+          src[j] = __float_as_uint(bdr_adjust(__uint_as_float(src[j]), sp[j], pv, s_new, R));
+        }
       }
     }
     pack16<BITS, 0>(src, out);
@@ -485,13 +522,7 @@ __device__ __forceinline__ void quantize16_rt(const float* sp, const float* inv1
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float pv = __builtin_fmaf(prev[j], s_old16[j], -bias * s_old16[j]);
-        float y = __uint_as_float(src[j]);
-        const float st = (y - kMagic) * s_new16[j];
-        const float x = sp[j];
-        if (x > pv && st < pv) y += 1.0f;
-        if (x < pv && st > pv) y -= 1.0f;
-        y = fminf(fmaxf(y, kMagic - r), kMagic + r);
-        src[j] = __float_as_uint(y);
+        src[j] = __float_as_uint(bdr_adjust(__uint_as_float(src[j]), sp[j], pv, s_new16[j], r));
       }
     }
   }

@@ -56,13 +56,7 @@ __device__ __forceinline__ void quantize16_cols(const float* sp, const float* in
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float pv = __builtin_fmaf(prev[j], s_old[j], -bias * s_old[j]);
-        float y = __uint_as_float(src[j]);
-        const float st = (y - kMagic) * s_new[j];
-        const float x = sp[j];
-        if (x > pv && st < pv) y += 1.0f;
-        if (x < pv && st > pv) y -= 1.0f;
-        y = fminf(fmaxf(y, kMagic - (float)R), kMagic + (float)R);
-        src[j] = __float_as_uint(y);
+        src[j] = __float_as_uint(bdr_adjust(__uint_as_float(src[j]), sp[j], pv, s_new[j], (float)R));
       }
     }
     pack16<BITS, 0>(src, out);

@@ -7,7 +7,8 @@
   every step through T = 1024 (B=256 INT4/INT8 mix), 512 (GLA, RTN and SR)
   and 256 (Mamba2-style, all 24 layer keys).
 * Reduced batch (heads are independent; the same per-head workload), every
-  head at every step through the same T.
+  head at every step through the same T, also with bounded directional
+  rounding on the Gated DeltaNet and GLA workloads.
 Set QSTATE_PARITY_EVERY_HEAD=1 to track every head of the full batch through
 T as well (minutes of host time).  Set QSTATE_PARITY_REPORT=<file> to append
 one JSON line per run."""
@@ -83,7 +84,7 @@ def test_config4_full_size_layers_to_T(first):
 
 
 @pytest.mark.parametrize("wid,B,rounding", [(2, 8, None), (3, 8, W.RTN), (3, 8, W.SR),
-                                            (5, 8, None)])
+                                            (5, 8, None), (2, 8, W.BDR), (3, 8, W.BDR)])
 def test_every_head_every_step_reduced_batch(wid, B, rounding):
     w = W.WORKLOADS[wid].scaled(B=B)
     rep = _run(w, w.steps, rounding, tag=f"B{B}-every")
