@@ -300,10 +300,23 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   float* lds_bo = lds;  // the leaving pair's key [dk], or every key [W][dk] (bypass merge)
   float* lds_c = lds + W * DK;
   float* lds_sa = lds_c + W;
+  float* lds_kq = lds_sa + W;  // the head's k, q and (GLA, KDA) alpha, [3][dk]
   constexpr bool merge = MERGE;
   float c_new, s_anew, inv_anew;
   window_prologue<MIXER, DK, W, MERGE>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
                                 lds_sa, c_new, s_anew, inv_anew);
+  // The rows read the head's vectors from LDS in every iteration instead of
+  // holding them in registers (2 or 3 x E floats per lane), which keeps the
+  // kernel within the registers of four waves per SIMD.
+  {
+    constexpr int NV = vector_decay(MIXER) ? 3 : 2;
+    const float* src[3] = {p.k + (size_t)sl.head * DK, p.q + (size_t)sl.head * DK,
+                           vector_decay(MIXER) ? p.alpha + (size_t)sl.head * DK : nullptr};
+#pragma unroll
+    for (int vi = 0; vi < NV; ++vi)
+      for (int f = lane; f < DK / 4; f += 64)
+        reinterpret_cast<float4*>(lds_kq + vi * DK)[f] = reinterpret_cast<const float4*>(src[vi])[f];
+  }
   __syncthreads();
   float ca[W], sa[W];  // by age: 0 = oldest (leaving), W-1 = newest before this step
 #pragma unroll
@@ -314,17 +327,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   }
   c_new = uniform(c_new);
   inv_anew = uniform(inv_anew);
-  // per-head vectors in the rows' lane layout, after the window work
-  float kk[E], qq[E], al[E];
-  loadv(p.k + (size_t)sl.head * DK + col0, kk);
-  loadv(p.q + (size_t)sl.head * DK + col0, qq);
-  if constexpr (vector_decay(MIXER)) {
-    loadv(p.alpha + (size_t)sl.head * DK + col0, al);
-  } else {
-#pragma unroll
-    for (int j = 0; j < E; ++j) al[j] = 0.0f;
-  }
-  asm volatile("" ::: "memory");
+  const float* lk = lds_kq + col0;
 
   const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
   for (int t = 0; t < n_trips; ++t) {
@@ -337,6 +340,10 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
       const float s_0 = ring[k].s0, s_1 = ring[k].s1, vrow = ring[k].v;
       uint32_t ab[4] = {0u, 0u, 0u, 0u};
       age_order<W>(ring[k].a, slot, ab);
+      asm volatile("" ::: "memory");  // read the head's vectors from LDS here, not once
+      float kk[E], al[E];
+      loadv(lk, kk);
+      if constexpr (vector_decay(MIXER)) loadv(lk + 2 * DK, al);
       float d[E];
       if constexpr (vector_decay(MIXER)) {
         dequant_lane<BITS, E>(w, s_0, s_1, d);
@@ -374,6 +381,8 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
           d[j] = fabsf(m[j]) >= thr ? d[j] + m[j] : d[j];
         }
         ring[k] = load(it + kPrefetch);
+        float qq[E];
+        loadv(lk + DK, qq);
         o = __builtin_fmaf(a_new, c_new, row_sum<LPR>(lane_dot(d, qq)));
       } else {
         // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A); its
@@ -392,6 +401,8 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
         }
         ring[k] = load(it + kPrefetch);
         // readout of the full state: H'q, the pairs that stay (oldest first), the new pair
+        float qq[E];
+        loadv(lk + DK, qq);
         o = row_sum<LPR>(lane_dot(d, qq));
 #pragma unroll
         for (int g = 1; g < W; ++g) {
@@ -540,7 +551,7 @@ __device__ __forceinline__ void aux_pw_head(const KParams& p, const Slice sl, fl
 
 template <int DK, int W>
 constexpr int window_lds_floats() {
-  return W * DK + 2 * W;
+  return W * DK + 2 * W + 3 * DK;  // keys, c, s_a, then the head's k, q, alpha
 }
 
 // MERGE: the low-rank bypass merge step (a kernel of its own, so that the
