@@ -42,11 +42,21 @@ ROUNDING_NAMES = {0: "RTN", 1: "SR", 2: "BDR"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """The library's source hash (every source and header it is built from,
-    and the compile flags): stored profiler counts apply only to that build."""
+def kernel_unit(w) -> str:
+    """The translation unit holding the step kernels of workload w."""
+    if w.window:
+        return f"qstate_window_dk{w.dk}_w{w.window}.hip"
+    if w.axis:
+        return f"qstate_key_dk{w.dk}.hip"
+    return f"qstate_value_dk{w.dk}.hip"
+
+
+def kernel_source_hash(w) -> str:
+    """The source hash of w's step kernels (their unit, the headers it
+    includes, the launch code and the compile flags): stored profiler counts
+    apply only while it is unchanged."""
     from bit_recurrent_state_amd import build
-    return build.source_hash()
+    return build.unit_hash(kernel_unit(w))
 
 
 def traffic_key(w) -> str:
@@ -66,7 +76,7 @@ def measured_traffic(w):
     except (OSError, ValueError):
         return None
     e = t.get("workloads", {}).get(traffic_key(w))
-    if not e or t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash(w):
         return None
     return e["hbm_bytes_per_launch"]
 
@@ -81,7 +91,7 @@ def measured_valu(w):
     except (OSError, ValueError):
         return None
     e = t.get("workloads", {}).get(traffic_key(w))
-    if not e or t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash(w):
         return None
     return e.get("valu_wave_insts_per_launch")
 

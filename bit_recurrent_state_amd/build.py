@@ -88,6 +88,37 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def unit_hash(unit: str) -> str:
+    """sha256[:16] of one kernel translation unit (a file name in csrc/), every
+    header it includes, directly or not, the host code that configures its
+    launches, and the compile flags: profiler counts taken on a kernel stay
+    valid while this hash does, whatever else in the library changes."""
+    import hashlib
+    import re
+    dirs = [CSRC, os.path.join(ROOT, "include")]
+    seen, todo = [], [unit, "qstate_dispatch.cpp", "qstate_api.cpp"]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        path = next((os.path.join(d, name) for d in dirs if os.path.exists(os.path.join(d, name))),
+                    None)
+        if path is None:
+            continue
+        seen.append(name)
+        with open(path, "rb") as fh:
+            text = fh.read()
+        todo += [m.decode() for m in re.findall(rb'#include "([^"]+)"', text)]
+    h = hashlib.sha256()
+    for name in sorted(seen):
+        path = next(os.path.join(d, name) for d in dirs if os.path.exists(os.path.join(d, name)))
+        h.update(name.encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    h.update("\0".join(FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
 def stale() -> bool:
     """True when the library is missing or was built from other sources or flags."""
     if not os.path.exists(LIB) or not os.path.exists(HASH_FILE):

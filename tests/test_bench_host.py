@@ -71,10 +71,10 @@ def test_profile_records_follow_the_kernel_source(monkeypatch):
     w = W.WORKLOADS[2]
     entry = rec["workloads"].get(bench.traffic_key(w))
     assert entry is not None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["kernel_source_sha256_16"])
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w_: entry["kernel_source_sha256_16"])
     assert bench.measured_traffic(w) == entry["hbm_bytes_per_launch"]
     assert bench.measured_valu(w) == entry.get("valu_wave_insts_per_launch")
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda w_: "0" * 16)
     assert bench.measured_traffic(w) is None
     assert bench.measured_valu(w) is None
 
@@ -84,8 +84,8 @@ def test_stored_records_are_calibrated():
     factors an in-place xor of known size gives on gfx950."""
     import bench
     rec = json.load(open(bench.TRAFFIC_FILE))
-    assert len(rec["kernel_source_sha256_16"]) == 16
     for key, e in rec["workloads"].items():
+        assert len(e["kernel_source_sha256_16"]) == 16, key
         assert e["hbm_bytes_per_launch"] > 0, key
         assert e["fetch_scale"] == pytest.approx(2.0, rel=1e-3), key
         assert e["write_scale"] == pytest.approx(1.0, rel=1e-3), key
@@ -102,6 +102,26 @@ def test_traffic_close_to_algorithmic_bytes(Q):
         e = rec[bench.traffic_key(w)]
         alg = bench.algorithmic_bytes(w, bench.block_bits(w, Q))
         assert 1.0 <= e["hbm_bytes_per_launch"] / alg < 1.10, (wid, e["hbm_bytes_per_launch"], alg)
+
+
+def test_unit_hash_follows_its_includes(tmp_path, monkeypatch):
+    """A kernel unit's hash covers the headers it includes and no others."""
+    from bit_recurrent_state_amd import build
+    src = tmp_path / "csrc"
+    inc = tmp_path / "include"
+    src.mkdir()
+    inc.mkdir()
+    (src / "a.hip").write_text('#include "h1.h"\n')
+    (src / "h1.h").write_text('#include "h2.h"\n')
+    (src / "h2.h").write_text("int x;\n")
+    (src / "other.h").write_text("int y;\n")
+    monkeypatch.setattr(build, "CSRC", str(src))
+    monkeypatch.setattr(build, "ROOT", str(tmp_path))
+    h0 = build.unit_hash("a.hip")
+    (src / "other.h").write_text("int z;\n")
+    assert build.unit_hash("a.hip") == h0
+    (src / "h2.h").write_text("int w;\n")
+    assert build.unit_hash("a.hip") != h0
 
 
 def test_more_than_one_gpu_is_refused():
