@@ -471,7 +471,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--rounding", type=int, default=None, help="override: 0 RTN, 1 SR, 2 BDR")
     ap.add_argument("--axis", type=int, default=0,
@@ -488,7 +488,7 @@ def main():
                     help="pre-generated input batches of at least this many MB")
     ap.add_argument("--cpu-seconds", type=float, default=2.0,
                     help="wall seconds of the CPU-reference sample on every host core")
-    ap.add_argument("--cpu-single-seconds", type=float, default=4.0,
+    ap.add_argument("--cpu-single-seconds", type=float, default=7.0,
                     help="wall seconds of the single-thread CPU-reference sample")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads, hot, FP32-state and ceiling figures")
@@ -544,6 +544,9 @@ def main():
                 for i in range(n_states * len(pool))]
 
     ms = timed(torch, launches, args.steps, args.warmup)
+    # the same launches again as 5 repetitions, for the spread (the value
+    # above stays the one timed region of exactly --steps steps)
+    reps = [timed(torch, launches, max(1, args.steps // 5), 0) for _ in range(5)]
     rf = roofline(nbytes, ms)
     rf["traffic"] = measured_traffic(w)
     gbps = rf["achieved"]
@@ -575,6 +578,8 @@ def main():
         },
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "repetitions": {"ms_per_step": reps, "median_ms_per_step": float(np.median(reps)),
+                        "steps_each": max(1, args.steps // 5)},
         "roofline": rf,
     }
     # The same launches against the vector-ALU issue rate (the INT4 + SR path
