@@ -97,8 +97,9 @@ struct LaneCodes {
 
 // Step (OP = kStep) or import (OP = kImport) of a quantized head with
 // key-axis groups.  LDS: partial column maxima, old scales, new scales and
-// inverse scales of the block's row groups.  BITS = 0: mixed widths.
-template <int OP, int MIXER, int RND, int DK, int BITS, int G>
+// inverse scales of the block's row groups, and the head's vectors.  BITS =
+// 0: mixed widths.
+template <int OP, int MIXER, int RND, int DK, int BITS, int G, bool PF>
 __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl, float* lds) {
   using K = KGeo<DK, G>;
   constexpr int E = K::E, LPR = K::LPR, RPW = K::RPW, NI = K::NI, RB = K::RB, NW = K::NW;
@@ -108,6 +109,7 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   float* so = pm + LG * PARTS * DK;       // [LG][DK] scales before the step
   float* sn = so + LG * DK;               // [LG][DK] new scales
   float* si = sn + LG * DK;               // [LG][DK] new inverse scales
+  float* skq = si + LG * DK;              // [3][DK] the head's k, q, alpha (PF)
 
   const int tid = threadIdx.x;
   const int wv = tid / 64;
@@ -122,16 +124,32 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   const uint32_t key =
       (RND == kSR) ? head_key(p, (uint32_t)sl.b, (uint32_t)sl.h) : 0u;
 
+  // PF (a step; see key_prefetch): the head's k, q and alpha go to LDS and
+  // are read there in every row iteration instead of being held in 2-3 x E
+  // registers per lane, and the freed registers hold the next block's codes,
+  // loaded while this block computes.  Otherwise the vectors stay in
+  // registers and each block is loaded when it starts.  The block loop's
+  // first barrier publishes the vectors.
+  static_assert(!PF || OP == kStep, "prefetch is a step layout");
   float kk[E], qq[E], al[E];
   float alpha_s = 0.0f, beta = 0.0f;
   const float* vh = nullptr;
   float* oh = nullptr;
   if constexpr (OP == kStep) {
-    loadv(p.k + (size_t)sl.head * DK + col0, kk);
-    loadv(p.q + (size_t)sl.head * DK + col0, qq);
-    if constexpr (vector_decay(MIXER)) {
-      loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+    if constexpr (PF) {
+      constexpr int NV = vector_decay(MIXER) ? 3 : 2;
+      const float* src3[3] = {p.k + (size_t)sl.head * DK, p.q + (size_t)sl.head * DK,
+                              vector_decay(MIXER) ? p.alpha + (size_t)sl.head * DK : nullptr};
+#pragma unroll
+      for (int vi = 0; vi < NV; ++vi)
+        for (int f = tid; f < DK / 4; f += 64 * NW)
+          reinterpret_cast<float4*>(skq + vi * DK)[f] = reinterpret_cast<const float4*>(src3[vi])[f];
     } else {
+      loadv(p.k + (size_t)sl.head * DK + col0, kk);
+      loadv(p.q + (size_t)sl.head * DK + col0, qq);
+      if constexpr (vector_decay(MIXER)) loadv(p.alpha + (size_t)sl.head * DK + col0, al);
+    }
+    if constexpr (!vector_decay(MIXER)) {
 #pragma unroll
       for (int j = 0; j < E; ++j) al[j] = 0.0f;
       alpha_s = p.alpha[sl.head];
@@ -141,6 +159,27 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     oh = p.o ? p.o + (size_t)sl.head * p.dv : nullptr;
   }
 
+  // This wave's rows of a block: base + wv*RB + it*RPW + rsub; every row of
+  // an iteration lies in one row group, and a group is wholly inside dv or
+  // wholly outside (G divides dv, RPW divides G).
+  auto load_block = [&](int base_, uint32_t (&w_)[NI][4], float (&v_)[NI]) {
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int row = min(base_ + wv * RB + it * RPW + rsub, p.dv - 1);
+      const uint8_t* src = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
+      if (lc.is8) {
+        const uint4 t = ld_stream(reinterpret_cast<const uint4*>(src));
+        w_[it][0] = t.x, w_[it][1] = t.y, w_[it][2] = t.z, w_[it][3] = t.w;
+      } else {
+        const uint2 t = ld_stream(reinterpret_cast<const uint2*>(src));
+        w_[it][0] = t.x, w_[it][1] = t.y, w_[it][2] = 0u, w_[it][3] = 0u;
+      }
+      v_[it] = vh[row];
+    }
+  };
+  uint32_t wc[NI][4] = {};
+  float vr[NI] = {};
+  if constexpr (PF) load_block(sl.r0, wc, vr);
   for (int base = sl.r0; base < sl.r1; base += BR) {
     // scales of the block's row groups before the step
     if constexpr (OP == kStep) {
@@ -149,26 +188,20 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
         so[t] = grow * G < p.dv ? hscales[(size_t)grow * DK + t % DK] : 0.0f;
       }
     }
-    // this wave's rows: base + wv*RB + it*RPW + rsub; every row of an
-    // iteration lies in one row group, and a group is wholly inside dv or
-    // wholly outside (G divides dv, RPW divides G)
-    uint32_t wc[NI][4] = {};
-    float vr[NI] = {};
+    // PF: the next block's codes and v (issued unconditionally, so that the
+    // waits on this block's loads stay exact: after the last block the same
+    // rows again, never used); otherwise this block's
+    uint32_t wn[NI][4] = {};
+    float vn[NI] = {};
+    if constexpr (PF)
+      load_block(base + BR < sl.r1 ? base + BR : base, wn, vn);
+    else if constexpr (OP == kStep)
+      load_block(base, wc, vr);
     float sp[NI][E];
+    if constexpr (OP == kImport) {
 #pragma unroll
-    for (int it = 0; it < NI; ++it) {
-      const int row = min(base + wv * RB + it * RPW + rsub, p.dv - 1);
-      if constexpr (OP == kStep) {
-        const uint8_t* src = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
-        if (lc.is8) {
-          const uint4 t = ld_stream(reinterpret_cast<const uint4*>(src));
-          wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = t.z, wc[it][3] = t.w;
-        } else {
-          const uint2 t = ld_stream(reinterpret_cast<const uint2*>(src));
-          wc[it][0] = t.x, wc[it][1] = t.y, wc[it][2] = 0u, wc[it][3] = 0u;
-        }
-        vr[it] = vh[row];
-      } else {
+      for (int it = 0; it < NI; ++it) {
+        const int row = min(base + wv * RB + it * RPW + rsub, p.dv - 1);
         loadv(p.src + ((size_t)sl.head * p.dv + row) * DK + col0, sp[it]);
       }
     }
@@ -183,6 +216,12 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       const bool last = NW > 1 ? it == NI - 1 : ((it + 1) * RPW) % G == 0;
       if constexpr (OP == kStep) {
         const int row = base + wv * RB + it * RPW + rsub;
+        if constexpr (PF) {
+          asm volatile("" ::: "memory");  // the head's vectors from LDS here, not held
+          lds_load(skq + col0, kk);
+          lds_load(skq + DK + col0, qq);
+          if constexpr (vector_decay(MIXER)) lds_load(skq + 2 * DK + col0, al);
+        }
         float sc[E];
         lds_load(so + lg * DK + col0, sc);
         float d[E];
@@ -272,6 +311,14 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       }
     }
     __syncthreads();  // LDS free for the next block
+    if constexpr (PF) {
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        vr[it] = vn[it];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wc[it][q] = wn[it][q];
+      }
+    }
   }
 }
 
@@ -330,16 +377,28 @@ __device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
 // spilled by the BDR and SR variants): the workgroup barriers of the column
 // reductions need the other waves to fill the SIMD, and measured, three
 // waves with spills beat two without by 8-12 %.
+// Whether a key-axis step stages the head's vectors in LDS and prefetches
+// the next block (measured per variant, same-box A/B): yes for the
+// mixed-width step (-16 %) and KDA (-6 %, three vectors held otherwise); no
+// for BDR (slower: it keeps the previous codes through the requantization
+// and sits at its register bound) and for the other one-width steps
+// (Gated DeltaNet unchanged, GLA 1.5 % slower).
+template <int OP, int MIXER, int RND, bool MIXED>
+constexpr bool key_prefetch() {
+  return OP == kStep && RND != kBDR && (MIXED || MIXER == kKDA);
+}
+
 template <int OP, int MIXER, int RND, int DK, int G>
 __global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) __attribute__((amdgpu_waves_per_eu(3)))
 void key_kernel(const KParams p) {
   using K = KGeo<DK, G>;
-  __shared__ float lds[K::LG * (K::PARTS + 3) * DK];
+  constexpr bool PF = key_prefetch<OP, MIXER, RND, false>();
+  __shared__ float lds[K::LG * (K::PARTS + 3) * DK + (PF ? 3 * DK : 0)];
   const Slice sl = wave_slice(p);
   if (p.int8_blocks[sl.h] != 0u)
-    key_quant_head<OP, MIXER, RND, DK, 8, G>(p, sl, lds);
+    key_quant_head<OP, MIXER, RND, DK, 8, G, PF>(p, sl, lds);
   else
-    key_quant_head<OP, MIXER, RND, DK, 4, G>(p, sl, lds);
+    key_quant_head<OP, MIXER, RND, DK, 4, G, PF>(p, sl, lds);
 }
 
 // A launch with heads of mixed widths: every head takes the per-block path
@@ -347,8 +406,9 @@ void key_kernel(const KParams p) {
 template <int OP, int MIXER, int RND, int DK, int G>
 __global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_mixed_kernel(const KParams p) {
   using K = KGeo<DK, G>;
-  __shared__ float lds[K::LG * (K::PARTS + 3) * DK];
-  key_quant_head<OP, MIXER, RND, DK, 0, G>(p, wave_slice(p), lds);
+  constexpr bool PF = key_prefetch<OP, MIXER, RND, true>();
+  __shared__ float lds[K::LG * (K::PARTS + 3) * DK + (PF ? 3 * DK : 0)];
+  key_quant_head<OP, MIXER, RND, DK, 0, G, PF>(p, wave_slice(p), lds);
 }
 
 template <int OP, int DK, int G>
