@@ -162,10 +162,12 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   // This wave's rows of a block: base + wv*RB + it*RPW + rsub; every row of
   // an iteration lies in one row group, and a group is wholly inside dv or
   // wholly outside (G divides dv, RPW divides G).
+  // (base_ < 0: every load from the slice's first row, a stand-in that costs
+  // one cache line per lane group)
   auto load_block = [&](int base_, uint32_t (&w_)[NI][4], float (&v_)[NI]) {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const int row = min(base_ + wv * RB + it * RPW + rsub, p.dv - 1);
+      const int row = base_ < 0 ? sl.r0 : min(base_ + wv * RB + it * RPW + rsub, p.dv - 1);
       const uint8_t* src = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
       if (lc.is8) {
         const uint4 t = ld_stream(reinterpret_cast<const uint4*>(src));
@@ -189,12 +191,12 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       }
     }
     // PF: the next block's codes and v (issued unconditionally, so that the
-    // waits on this block's loads stay exact: after the last block the same
-    // rows again, never used); otherwise this block's
+    // waits on this block's loads stay exact: after the last block a
+    // stand-in that is never used); otherwise this block's
     uint32_t wn[NI][4] = {};
     float vn[NI] = {};
     if constexpr (PF)
-      load_block(base + BR < sl.r1 ? base + BR : base, wn, vn);
+      load_block(base + BR < sl.r1 ? base + BR : -1, wn, vn);
     else if constexpr (OP == kStep)
       load_block(base, wc, vr);
     float sp[NI][E];
