@@ -179,11 +179,14 @@ __device__ __forceinline__ void persist_class(const KParams& p, PState<MIXER, DK
   if (ps.cur.b < 0 || ps.cur.is8 != IS8) return;
 
   // Lane data of one row of a unit.  Rows past the head's end re-read its
-  // last row and are never stored; so are the rows a ring slot loads when no
-  // unit of this width follows.
+  // last row and are never stored.  it < 0: a stand-in load of row ur0 by
+  // every lane of a row group, for the ring slots refilled when no unit of
+  // this width follows (never computed; one cache line per lane group, where
+  // loading the rows past the unit read 11 MB more per headline launch; the
+  // loads stay unconditional so the waits on the ring stay exact).
   auto load = [&](int ub, int uh, int ur0, int it) {
     RowIn in;
-    const int row = min(ur0 + it * RPW + rsub, p.dv - 1);
+    const int row = it < 0 ? ur0 : min(ur0 + it * RPW + rsub, p.dv - 1);
     const size_t head = (size_t)ub * p.H + uh;
     const uint8_t* hc = reinterpret_cast<const uint8_t*>(p.state) + head_code_offset(p, ub, uh);
     const float* hs = p.scales + head * p.dv * ngr;
@@ -218,7 +221,7 @@ __device__ __forceinline__ void persist_class(const KParams& p, PState<MIXER, DK
     for (int trip = 0; trip < TRIPS; ++trip) {
       // The slots refilled in this trip feed the next one: cur's next trip,
       // or in cur's last trip nxt's first (without a next unit of this width,
-      // clamped rows of cur's head that are never computed).
+      // stand-in loads that are never computed).
       const bool to_next = trip + 1 == TRIPS && next_same;
       const int rb = to_next ? ps.nxt.b : ps.cur.b;  // values, not a reference: keeps ps in registers
       const int rh = to_next ? ps.nxt.h : ps.cur.h;
@@ -255,7 +258,8 @@ __device__ __forceinline__ void persist_class(const KParams& p, PState<MIXER, DK
         }
 #pragma unroll
         for (int j = 0; j < E; ++j) d[j] = __builtin_fmaf(wt, kk[j], d[j]);
-        ring[k] = load(rb, rh, rr0, rbase + k);  // nothing of the slot is live any more
+        // nothing of the slot is live any more
+        ring[k] = load(rb, rh, rr0, trip + 1 == TRIPS && !next_same ? -1 : rbase + k);
         float qq[E];
         loadv(lk + DK, qq);
         const float o = row_sum<LPR>(lane_dot(d, qq));
