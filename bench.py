@@ -60,9 +60,17 @@ def kernel_source_hash(w) -> str:
 
 
 def traffic_key(w) -> str:
+    """The record key of w's profiler counts: workload, rounding, axis, window
+    and bypass, plus the batch and width policy where they differ from the
+    workload's own (records are per shape and width mix)."""
+    import workloads as W
     key = f"{w.name}|{ROUNDING_NAMES[w.rounding]}|{'key' if w.axis else 'value'}-axis"
     key += f"|window{w.window}" if w.window else ""
-    return key + ("|lrb" if w.window_merge else "")
+    key += "|lrb" if w.window_merge else ""
+    base = W.WORKLOADS[w.wid]
+    key += f"|B{w.B}" if w.B != base.B else ""
+    key += f"|bits={w.bits_policy}" if w.bits_policy != base.bits_policy else ""
+    return key
 
 
 def measured_traffic(w):

@@ -165,3 +165,16 @@ def test_cpu_baseline_reports_every_core_and_one(monkeypatch):
     assert r["single_thread"]["cores"] == 1
     assert r["value"] > 0 and r["single_thread"]["value"] > 0
     assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+
+
+def test_profile_records_are_per_shape_and_width_mix():
+    """A run with another batch or width policy never picks up the record of
+    the workload's own shape and widths."""
+    import bench
+    import workloads as W
+    w = W.WORKLOADS[2]
+    keys = {bench.traffic_key(x) for x in (w, w.scaled(B=8), w.scaled(bits_policy="int8"),
+                                           w.scaled(rounding=W.RTN), w.scaled(axis=1),
+                                           w.scaled(window=8))}
+    assert len(keys) == 6
+    assert bench.traffic_key(w) == "gdn_b256_h32_d128_int4mix_g32_sr|SR|value-axis"
