@@ -162,12 +162,12 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   // This wave's rows of a block: base + wv*RB + it*RPW + rsub; every row of
   // an iteration lies in one row group, and a group is wholly inside dv or
   // wholly outside (G divides dv, RPW divides G).
-  // (base_ < 0: every load from the slice's first row, a stand-in that costs
-  // one cache line per lane group)
-  auto load_block = [&](int base_, uint32_t (&w_)[NI][4], float (&v_)[NI]) {
+  // (standin: every load from the slice's first row instead, a stand-in that
+  // costs one cache line per lane group)
+  auto load_block = [&](int base_, bool standin, uint32_t (&w_)[NI][4], float (&v_)[NI]) {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const int row = base_ < 0 ? sl.r0 : min(base_ + wv * RB + it * RPW + rsub, p.dv - 1);
+      const int row = standin ? sl.r0 : min(base_ + wv * RB + it * RPW + rsub, p.dv - 1);
       const uint8_t* src = hcodes + (size_t)row * lc.row_bytes + lc.lane_off;
       if (lc.is8) {
         const uint4 t = ld_stream(reinterpret_cast<const uint4*>(src));
@@ -181,7 +181,7 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   };
   uint32_t wc[NI][4] = {};
   float vr[NI] = {};
-  if constexpr (PF) load_block(sl.r0, wc, vr);
+  if constexpr (PF) load_block(sl.r0, false, wc, vr);
   for (int base = sl.r0; base < sl.r1; base += BR) {
     // scales of the block's row groups before the step
     if constexpr (OP == kStep) {
@@ -196,9 +196,9 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     uint32_t wn[NI][4] = {};
     float vn[NI] = {};
     if constexpr (PF)
-      load_block(base + BR < sl.r1 ? base + BR : -1, wn, vn);
+      load_block(base + BR, base + BR >= sl.r1, wn, vn);
     else if constexpr (OP == kStep)
-      load_block(base, wc, vr);
+      load_block(base, false, wc, vr);
     float sp[NI][E];
     if constexpr (OP == kImport) {
 #pragma unroll
@@ -380,14 +380,15 @@ __device__ __forceinline__ void key_aux_head(const KParams& p, const Slice sl) {
 // reductions need the other waves to fill the SIMD, and measured, three
 // waves with spills beat two without by 8-12 %.
 // Whether a key-axis step stages the head's vectors in LDS and prefetches
-// the next block (measured per variant, same-box A/B): yes for the
-// mixed-width step (-16 %) and KDA (-6 %, three vectors held otherwise); no
-// for BDR (slower: it keeps the previous codes through the requantization
-// and sits at its register bound) and for the other one-width steps
-// (Gated DeltaNet unchanged, GLA 1.5 % slower).
+// the next block (measured per variant, same-box A/B): yes for every step
+// but two: BDR (slower: it keeps the previous codes through the
+// requantization and sits at its register bound) and one-width GLA with
+// round to nearest (3 % slower; its INT8 rows already keep enough loads in
+// flight).  Gains: mixed widths -16 %, GLA SR -13 %, Gated DeltaNet SR -9 %,
+// KDA -7 %.
 template <int OP, int MIXER, int RND, bool MIXED>
 constexpr bool key_prefetch() {
-  return OP == kStep && RND != kBDR && (MIXED || MIXER == kKDA);
+  return OP == kStep && RND != kBDR && (MIXED || !(MIXER == kGLA && RND == kRTN));
 }
 
 template <int OP, int MIXER, int RND, int DK, int G>
