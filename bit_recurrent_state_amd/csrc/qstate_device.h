@@ -424,6 +424,38 @@ __device__ __forceinline__ void sr16_cols(const float* sp, const float* inv16, u
   }
 }
 
+// The same for 16 elements of a lane whose width is chosen at run time, with
+// one instruction sequence for both widths: (bits(y) << sh) + (R16 | add)
+// (one shift-add and one byte permute), sh = 1 and add = 2^23 for an 8-bit
+// lane, 0 and 0 for a 4-bit one: that is 2 bits(y) + R16 + 2^23 and
+// bits(y) + R16, the two forms of sr_word, so byte 2 is the code either way
+// and lanes of the two widths no longer run both forms and a select.
+__device__ __forceinline__ void sr16_rt(const float* sp, const float* inv16, uint32_t key,
+                                        uint32_t block, bool is8, uint32_t* src) {
+  uint32_t w[8];
+  block_words(key, block, w);
+  const float scale_f = is8 ? 32768.0f : 65536.0f;
+  const uint32_t sh = is8 ? 1u : 0u;
+  const uint32_t add = is8 ? 0x00800000u : 0u;
+  float imax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) imax = fmaxf(imax, inv16[j]);
+  float y[16];
+  if (__builtin_expect(imax <= 0x1p100f, 1)) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = __builtin_fmaf(sp[j], inv16[j] * scale_f, kMagic);
+  } else {  // a tiny-magnitude group, where inv * 2^f could overflow: same exact product
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = __builtin_fmaf(sp[j] * scale_f, inv16[j], kMagic);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    // R16 (the low or high half of the word) with add's byte 2 above it
+    const uint32_t r = __builtin_amdgcn_perm(add, w[j >> 1], (j & 1) ? 0x0C060302u : 0x0C060100u);
+    src[j] = (__float_as_uint(y[j]) << sh) + r;
+  }
+}
+
 // Requantize the lane's E elements of the updated row S' into 16 bytes of
 // codes.  LPG = 0: two groups per lane (INT4 with G = 16, one per chunk);
 // otherwise one group spanning LPG lanes.  s0/s1: the scales of the lane's
@@ -510,7 +542,7 @@ __device__ __forceinline__ void quantize16_rt(const float* sp, const float* inv1
                                               bool is8, uint32_t* out) {
   uint32_t src[16];
   if constexpr (RND == kSR) {
-    sr16_cols(sp, inv16, key, block, is8, src);
+    sr16_rt(sp, inv16, key, block, is8, src);
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) src[j] = __float_as_uint(__builtin_fmaf(sp[j], inv16[j], kMagic));

@@ -164,3 +164,26 @@ def test_kernel_float_identities():
         assert r.returncode == 0, r.stdout
         assert lines == {"identity1": "0", "identity2": "0", "identity3": "0", "identity4": "0",
                          "identity5": "0"}
+
+
+def test_one_stochastic_rounding_form_for_both_widths():
+    """Lanes whose width is chosen at run time compute the stochastic-rounding
+    word as (bits(y) << sh) + (R16 | add), sh = 1 and add = 2^23 for 8 bits,
+    0 and 0 for 4 bits, with R16 | add formed by one byte permute.  That equals
+    the one-width forms 2 bits(y) + R16 + 2^23 and bits(y) + R16 modulo 2^32
+    (R16 < 2^16 leaves bit 23 free), checked here over every R16 for sampled
+    y of the constant's binade, byte 2 and its low nibble."""
+    import numpy as np
+    rng = np.random.default_rng(11)
+    magic = 0x4B400000
+    ys = np.concatenate([magic + rng.integers(-(1 << 22), 1 << 22, 2000),
+                         magic + np.array([-(1 << 22), (1 << 22) - 1, 0, 1, -1])]).astype(np.int64)
+    r16 = np.arange(1 << 16, dtype=np.int64)
+    m32 = (1 << 32) - 1
+    for y in ys:
+        one8 = ((2 * y + r16 + (1 << 23)) & m32) >> 16 & 0xFF
+        rt8 = (((y << 1) + (r16 | (1 << 23))) & m32) >> 16 & 0xFF
+        assert np.array_equal(one8, rt8), hex(y)
+        one4 = ((y + r16) & m32) >> 16 & 0xF
+        rt4 = (((y << 0) + (r16 | 0)) & m32) >> 16 & 0xF
+        assert np.array_equal(one4, rt4), hex(y)
