@@ -8,7 +8,8 @@
   and 256 (Mamba2-style, all 24 layer keys).
 * Reduced batch (heads are independent; the same per-head workload), every
   head at every step through the same T, also with bounded directional
-  rounding on the Gated DeltaNet and GLA workloads.
+  rounding on the Gated DeltaNet and GLA workloads, with key-axis scale
+  groups, and with per-channel widths.
 Set QSTATE_PARITY_EVERY_HEAD=1 to track every head of the full batch through
 T as well (minutes of host time).  Set QSTATE_PARITY_REPORT=<file> to append
 one JSON line per run."""
@@ -88,6 +89,24 @@ def test_config4_full_size_layers_to_T(first):
 def test_every_head_every_step_reduced_batch(wid, B, rounding):
     w = W.WORKLOADS[wid].scaled(B=B)
     rep = _run(w, w.steps, rounding, tag=f"B{B}-every")
+    assert rep.head_steps == w.B * w.H * w.steps
+
+
+@pytest.mark.parametrize("wid,B,rounding", [(3, 8, W.RTN), (3, 8, W.SR), (2, 8, None),
+                                            (5, 8, None), (6, 8, None)])
+def test_key_axis_every_head_every_step_reduced_batch(wid, B, rounding):
+    """Key-axis scale groups (the block-prefetching kernels and the plain
+    one) over the workloads' whole step counts, every head."""
+    w = W.WORKLOADS[wid].scaled(B=B, axis=1)
+    rep = _run(w, w.steps, rounding, tag=f"B{B}-every-keyaxis")
+    assert rep.head_steps == w.B * w.H * w.steps
+
+
+def test_channel_bits_every_head_every_step_reduced_batch():
+    """Per-channel widths (lanes of both widths in every wave) over the
+    workload's whole step count, every head."""
+    w = W.WORKLOADS[6].scaled(B=8)
+    rep = _run(w, w.steps, tag="B8-every")
     assert rep.head_steps == w.B * w.H * w.steps
 
 
