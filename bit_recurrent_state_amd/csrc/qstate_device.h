@@ -338,15 +338,38 @@ __device__ __forceinline__ uint32_t bdr_adjust_bits(uint32_t ybits, float x, flo
   return (uint32_t)min(max((int)ybits - t, lo), hi);
 }
 
+// The same step for the persistent kernel's INT4 lanes, in fewer
+// instructions: the [-1, 1] clamp is one v_med3_i32 (the compiler otherwise
+// folds the negation into a shift, a compare and a select), and the final
+// clamp to [-r, r] is left out (CLAMP = false) where no group of the wave
+// has an absmax m below 2^-100.  It can only act for such m: for m >= 2^-100,
+// RN(r * RN(m / r)) is m or a float neighbour of m (every mantissa checked
+// for r = 7 and 127), so no stored value lies strictly between the value of
+// code +-r and an |x| <= m, and no step leaves [-r, r].
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t bdr_step_fast(uint32_t ybits, float x, float pv, float s_new,
+                                                  float r) {
+  const float st = (__uint_as_float(ybits) - kMagic) * s_new;
+  const float m = __builtin_amdgcn_fmed3f(pv - x, st - pv, 0.0f);
+  int t;
+  asm("v_med3_i32 %0, %1, -1, 1" : "=v"(t) : "v"(__float_as_int(m)));
+  const int y = (int)ybits - t;
+  if constexpr (!CLAMP) return (uint32_t)y;
+  const int lo = __float_as_int(kMagic - r), hi = __float_as_int(kMagic + r);
+  return (uint32_t)min(max(y, lo), hi);
+}
+
 // Requantize one 16-element chunk with inverse scale inv into 16 packed codes
 // (four words for INT8, two for INT4).  block: the chunk's 16-element block
 // index in the head (stochastic rounding).  wprev / s_old: the chunk's codes
 // and scale before the step, s_new its new scale (bounded directional
-// rounding).
-template <int BITS, int RND>
+// rounding).  FAST (INT4 BDR of the persistent step): bdr_step_fast, with the
+// clamp to [-r, r] only when tiny, i.e. when some group of the wave has an
+// absmax below 2^-100 or NaN (wave-uniform).
+template <int BITS, int RND, bool FAST = false>
 __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t key, uint32_t block,
                                            const uint32_t* wprev, float s_old, float s_new,
-                                           uint32_t* out) {
+                                           uint32_t* out, bool tiny = true) {
   uint32_t src[16];
   if constexpr (RND == kSR) {
     constexpr float scale_f = BITS == 8 ? 32768.0f : 65536.0f;  // 2^f
@@ -371,7 +394,33 @@ __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t 
     if constexpr (RND == kBDR) {
       // prev = c*s_old exactly as stored
       constexpr float R = (float)((1 << (BITS - 1)) - 1);
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 4 && FAST) {
+        // widened as in dequant_lane, four elements at a time, each four
+        // adjusted as soon as they are widened (fewer live registers)
+        const float u = s_old * 512.0f, nb = -8.0f * s_old;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t wq = wprev[q];
+          asm("" : "+v"(wq));
+          const uint32_t lo = (wq & 0x0F0F0F0Fu) ^ 0x08080808u;
+          const uint32_t hi = ((wq >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto e = h ? __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true)
+                             : __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+            const auto o = h ? __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true)
+                             : __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+            const float pv4[4] = {__builtin_fmaf(e[0], u, nb), __builtin_fmaf(o[0], u, nb),
+                                  __builtin_fmaf(e[1], u, nb), __builtin_fmaf(o[1], u, nb)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = 8 * q + 4 * h + i;
+              src[j] = tiny ? bdr_step_fast<true>(src[j], sp[j], pv4[i], s_new, R)
+                            : bdr_step_fast<false>(src[j], sp[j], pv4[i], s_new, R);
+            }
+          }
+        }
+      } else if constexpr (BITS == 4) {
         // widened as the step's dequantization widens INT4 codes; the words
         // pass through an empty asm so that the widening is redone here
         // rather than kept live from the dequantization (E more registers
@@ -461,7 +510,7 @@ __device__ __forceinline__ void sr16_rt(const float* sp, const float* inv16, uin
 // otherwise one group spanning LPG lanes.  s0/s1: the scales of the lane's
 // groups (in: before the step, used by bounded directional rounding; out:
 // the new ones).  wprev: the lane's four code words before the step.
-template <int BITS, int RND, int E, int LPG>
+template <int BITS, int RND, int E, int LPG, bool FAST = false>
 __device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t key, uint32_t block0,
                                                const uint32_t* wprev, float& s0, float& s1) {
   constexpr int R = (1 << (BITS - 1)) - 1;
@@ -482,10 +531,15 @@ __device__ __forceinline__ uint4 quantize_lane(const float (&sp)[E], uint32_t ke
     group_scale<R>(m0, s0, inv0);
     s1 = s0, inv1 = inv0;
   }
+  bool tiny = true;
+  if constexpr (FAST && RND == kBDR && BITS == 4) {
+    const float mmin = LPG == 0 ? fminf(m0, m1) : m0;
+    tiny = __builtin_amdgcn_ballot_w64(!(mmin >= 0x1p-100f)) != 0;
+  }
   uint32_t o[4];
-  quantize16<BITS, RND>(sp, inv0, key, block0, wprev, so0, s0, o);
+  quantize16<BITS, RND, FAST>(sp, inv0, key, block0, wprev, so0, s0, o, tiny);
   if constexpr (E == 32)
-    quantize16<BITS, RND>(sp + 16, inv1, key, block0 + 1, wprev + 2, so1, s1, o + 2);
+    quantize16<BITS, RND, FAST>(sp + 16, inv1, key, block0 + 1, wprev + 2, so1, s1, o + 2, tiny);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 

@@ -265,7 +265,7 @@ __device__ __forceinline__ void persist_class(const KParams& p, PState<MIXER, DK
         const float o = row_sum<LPR>(lane_dot(d, qq));
         float s0 = s_0, s1 = s_1;
         const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
-        const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
+        const uint4 packed = quantize_lane<BITS, RND, E, LPG, true>(d, key, block0, w, s0, s1);
         if (store_ok) {
           st_stream(reinterpret_cast<uint4*>(hcodes + (uint32_t)(row * Gm::ROW_BYTES + lr * 16)), packed);
           if constexpr (two_groups) {

@@ -187,3 +187,86 @@ def test_one_stochastic_rounding_form_for_both_widths():
         one4 = ((y + r16) & m32) >> 16 & 0xF
         rt4 = (((y << 0) + (r16 | 0)) & m32) >> 16 & 0xF
         assert np.array_equal(one4, rt4), hex(y)
+
+
+BDR_SRC = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+static float f_of(uint32_t u){float f; memcpy(&f,&u,4); return f;}
+static uint32_t u_of(float f){uint32_t u; memcpy(&u,&f,4); return u;}
+static uint64_t s = 0x9E3779B97F4A7C15ull;
+static uint32_t rnd(void){ s ^= s << 13; s ^= s >> 7; s ^= s << 17; return (uint32_t)(s >> 11); }
+static float med3f(float a, float b, float c){ return fmaxf(fminf(a, b), fminf(fmaxf(a, b), c)); }
+static int med3i(int a, int b, int c){ int lo = a < b ? a : b, hi = a < b ? b : a;
+  return c < lo ? lo : (c > hi ? hi : c); }
+static float inv_rz(float m, float r){ float v = (float)((double)r / (double)m);
+  while ((double)v * (double)m > (double)r) v = nextafterf(v, 0.0f); return v; }
+int main(void){
+  long bad1 = 0, bad2 = 0, steps = 0;
+  const float rs[2] = {7.0f, 127.0f};
+  /* 1: RN(r * RN(m / r)) is m or a float neighbour of m, every mantissa of [1, 2) */
+  for (int t = 0; t < 2; ++t)
+    for (uint32_t mant = 0; mant < (1u << 23); ++mant) {
+      const float m = f_of((127u << 23) | mant), r = rs[t];
+      const float tr = r * (m / r);
+      if (tr != m && tr != nextafterf(m, 0.0f) && tr != nextafterf(m, 1e30f)) {
+        if (bad1 < 5) printf("neighbour r=%g m=%a\n", r, m); ++bad1; }
+    }
+  /* 2: the definition (round to nearest, one step toward the update where the
+     stored value p lies strictly between n*s_new and x, clamp to [-r, r])
+     against the unclamped branch-free form (y - med3_i32(bits(med3(p - x,
+     n*s_new - p, 0)), -1, 1)) for groups with absmax m >= 2^-100, x drawn
+     near the group's edges and p near the grid values around x */
+  for (int t = 0; t < 2; ++t)
+    for (int it = 0; it < 4000000; ++it) {
+      const float r = rs[t];
+      const float m = f_of(((uint32_t)(27 + rnd() % 200) << 23) | (rnd() & 0x7fffffu));
+      const float s_new = m / r, inv = inv_rz(m, r);
+      const uint32_t k = rnd() % 4;
+      float x = k == 0 ? m : (k == 1 ? -m : m * ((float)(rnd() & 0xffffff) / 8388608.0f - 1.0f));
+      if (rnd() & 1) x = nextafterf(x, 0.0f);
+      const float y = fmaf(x, inv, 12582912.0f);
+      const int n = (int)(u_of(y) - 0x4B400000u);
+      const float grid = (float)n * s_new;
+      float p;
+      const uint32_t c = rnd() % 6;
+      if (c == 0) p = nextafterf(grid, 1e30f); else if (c == 1) p = nextafterf(grid, -1e30f);
+      else if (c == 2) p = nextafterf(x, 1e30f); else if (c == 3) p = nextafterf(x, -1e30f);
+      else p = grid + (x - grid) * ((float)(rnd() & 0xffff) / 65536.0f) * (c == 4 ? 1.0f : 2.0f);
+      int want = n;
+      if (x > p && grid < p) want += 1;
+      if (x < p && grid > p) want -= 1;
+      want = want < -(int)r ? -(int)r : (want > (int)r ? (int)r : want);
+      const float mm = med3f(p - x, (y - 12582912.0f) * s_new - p, 0.0f);
+      int sm; memcpy(&sm, &mm, 4);
+      const int got = (int)u_of(y) - med3i(sm, -1, 1) - 0x4B400000;
+      if (got != n) ++steps;
+      if (got != want) { if (bad2 < 5) printf("bdr r=%g m=%a x=%a p=%a\n", r, m, x, p); ++bad2; }
+    }
+  printf("bdr1 %ld\nbdr2 %ld\nsteps %ld\n", bad1, bad2, steps);
+  return (bad1 || bad2) ? 1 : 0;
+}
+"""
+
+
+def test_bdr_unclamped_step_for_normal_groups():
+    """The persistent step's INT4 BDR leaves out the clamp to [-r, r] unless
+    some group of the wave has an absmax below 2^-100: RN(r * RN(m / r)) is m
+    or a float neighbour of m for every mantissa (so, by exact power-of-two
+    scaling, for every m >= 2^-100, where m / r stays normal), which leaves no
+    stored value strictly between the value of code +-r and an |x| <= m; and
+    on sampled groups the branch-free unclamped form equals the definition
+    (round to nearest, one step toward the update, clamp)."""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "bdr.c")
+        exe = os.path.join(d, "bdr")
+        open(c, "w").write(BDR_SRC)
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-o", exe, c, "-lm"],
+                       check=True)
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+        lines = dict(l.split() for l in r.stdout.splitlines())
+        assert r.returncode == 0, r.stdout
+        assert lines["bdr1"] == "0" and lines["bdr2"] == "0"
+        assert int(lines["steps"]) > 100000  # the samples do exercise the directional step
