@@ -413,7 +413,10 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
       }
       float s0 = s_0, s1 = s_1;
       const uint32_t block0 = (uint32_t)((row * DK + col0) >> 4);
-      const uint4 packed = quantize_lane<BITS, RND, E, LPG>(d, key, block0, w, s0, s1);
+      // the INT4 BDR fast path where the kernel already runs at three waves
+      // per SIMD (delta-rule mixers), whose register bound leaves room for it
+      constexpr bool FAST = delta_rule(MIXER);
+      const uint4 packed = quantize_lane<BITS, RND, E, LPG, FAST>(d, key, block0, w, s0, s1);
       if (store_ok) {
         st_stream(reinterpret_cast<uint4*>(hcodes + (size_t)row * Gm::ROW_BYTES + lr * 16), packed);
         if constexpr (two_groups) {
