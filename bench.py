@@ -76,8 +76,8 @@ def traffic_key(w) -> str:
 def measured_traffic(w):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     counts of this workload, rounding and group axis (scaled by the same
-    counters on an in-place xor of known size); None when they were not taken
-    or the kernel source changed since."""
+    counters on the library's 2 GiB in-place read-modify-write kernel); None
+    when they were not taken or the kernel source changed since."""
     try:
         import json as _j
         t = _j.load(open(TRAFFIC_FILE))

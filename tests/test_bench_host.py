@@ -81,7 +81,8 @@ def test_profile_records_follow_the_kernel_source(monkeypatch):
 
 def test_stored_records_are_calibrated():
     """Each stored record scales FETCH_SIZE by 2 and WRITE_SIZE by 1, the
-    factors an in-place xor of known size gives on gfx950."""
+    factors the library's 2 GiB in-place read-modify-write kernel gives on
+    gfx950."""
     import bench
     rec = json.load(open(bench.TRAFFIC_FILE))
     for key, e in rec["workloads"].items():
