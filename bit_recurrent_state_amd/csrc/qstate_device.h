@@ -318,8 +318,9 @@ __device__ __forceinline__ float bdr_adjust(float y, float x, float pv, float s_
 }
 
 // The same decision without compares, on the bit pattern of y, for the INT4
-// lanes of the value-axis step (measured faster there than the compares,
-// which the INT8 and key-axis paths keep).  With a = pv - x and
+// lanes of the steps that do not take bdr_step_fast below (measured faster
+// there than the compares, which the INT8, key-axis and mixed-width paths
+// keep).  With a = pv - x and
 // b = n*s_new - pv (signs exact), pv lies strictly between n*s_new and x
 // exactly when a and b are nonzero with one sign, the sign opposite to the
 // step; med3(a, b, 0) is then the one of them nearer zero, and zero
@@ -338,14 +339,15 @@ __device__ __forceinline__ uint32_t bdr_adjust_bits(uint32_t ybits, float x, flo
   return (uint32_t)min(max((int)ybits - t, lo), hi);
 }
 
-// The same step for the persistent kernel's INT4 lanes, in fewer
-// instructions: the [-1, 1] clamp is one v_med3_i32 (the compiler otherwise
-// folds the negation into a shift, a compare and a select), and the final
-// clamp to [-r, r] is left out (CLAMP = false) where no group of the wave
-// has an absmax m below 2^-100.  It can only act for such m: for m >= 2^-100,
-// RN(r * RN(m / r)) is m or a float neighbour of m (every mantissa checked
-// for r = 7 and 127), so no stored value lies strictly between the value of
-// code +-r and an |x| <= m, and no step leaves [-r, r].
+// The same step in fewer instructions (INT4 lanes of the persistent step and
+// of the delta-rule window steps): the [-1, 1] clamp is one v_med3_i32 (the
+// compiler otherwise folds the negation into a shift, a compare and a
+// select), and the final clamp to [-r, r] is left out (CLAMP = false) where
+// no group of the wave has an absmax m below 2^-100.  It can only act for
+// such m: for m >= 2^-100, RN(r * RN(m / r)) is m or a float neighbour of m
+// (every mantissa checked for r = 7 and 127), so no stored value lies
+// strictly between the value of code +-r and an |x| <= m, and no step
+// leaves [-r, r].
 template <bool CLAMP>
 __device__ __forceinline__ uint32_t bdr_step_fast(uint32_t ybits, float x, float pv, float s_new,
                                                   float r) {
@@ -363,9 +365,9 @@ __device__ __forceinline__ uint32_t bdr_step_fast(uint32_t ybits, float x, float
 // (four words for INT8, two for INT4).  block: the chunk's 16-element block
 // index in the head (stochastic rounding).  wprev / s_old: the chunk's codes
 // and scale before the step, s_new its new scale (bounded directional
-// rounding).  FAST (INT4 BDR of the persistent step): bdr_step_fast, with the
-// clamp to [-r, r] only when tiny, i.e. when some group of the wave has an
-// absmax below 2^-100 or NaN (wave-uniform).
+// rounding).  FAST (INT4 BDR of the persistent and delta-rule window steps):
+// bdr_step_fast, with the clamp to [-r, r] only when tiny, i.e. when some
+// group of the wave has an absmax below 2^-100 or NaN (wave-uniform).
 template <int BITS, int RND, bool FAST = false>
 __device__ __forceinline__ void quantize16(const float* sp, float inv, uint32_t key, uint32_t block,
                                            const uint32_t* wprev, float s_old, float s_new,
