@@ -272,6 +272,37 @@ def test_full_size_sampled_heads(wid):
     _run(w, FULL[wid], heads=heads)
 
 
+@pytest.mark.parametrize("window", [0, 8])
+def test_bdr_tiny_and_ordinary_groups(window):
+    """INT4 bounded directional rounding takes the clamp to [-r, r] only in
+    waves holding a group below 2^-100: heads near 1e-35 beside ordinary
+    heads (persistent step, and the window step of Gated DeltaNet), every
+    head at every step bit-exact."""
+    class TinyRun(Run):
+        """v scaled by 1e-35 for the heads with even b + h: their states and
+        group maxima stay far below 2^-100."""
+
+        def inputs(self, t):
+            q, k, v, alpha, beta = super().inputs(t)
+            v = v.copy()
+            for b in range(self.w.B):
+                for h in range(self.w.H):
+                    if (b + h) % 2 == 0:
+                        v[b, h] *= np.float32(1e-35)
+            return q, k, v, alpha, beta
+
+    w = W.Workload(98, "bdr_tiny", W.GDN, 2, 4, 128, 64, 32, 6, 8, W.BDR, "int8").scaled(
+        window=window)
+    r = TinyRun(w, head_bits_override=np.array([4, 4, 4, 8], np.uint8), seed=3)
+    log(f"[case] bdr tiny and ordinary groups window={window}")
+    r.warmup_and_import()
+    for _ in range(w.steps):
+        r.step()
+    r.dequant_check()
+    r.close()
+    assert r.rep.steps == w.steps
+
+
 def _small_case(mixer=W.GDN, rounding=W.SR, bits=(4, 8, 8)):
     return W.Workload(97, "small", mixer, 2, len(bits), 128, 48, 32, 6, 3, rounding, "int8"), \
         np.array(bits, np.uint8)
