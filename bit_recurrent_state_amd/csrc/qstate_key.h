@@ -105,11 +105,15 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   constexpr int E = K::E, LPR = K::LPR, RPW = K::RPW, NI = K::NI, RB = K::RB, NW = K::NW;
   constexpr int BR = K::BR, LG = K::LG, PARTS = K::PARTS;
   const uint32_t mask = p.int8_blocks[sl.h];
-  float* pm = lds;                        // [LG][PARTS][DK]
-  float* so = pm + LG * PARTS * DK;       // [LG][DK] scales before the step
-  float* sn = so + LG * DK;               // [LG][DK] new scales
-  float* si = sn + LG * DK;               // [LG][DK] new inverse scales
-  float* skq = si + LG * DK;              // [3][DK] the head's k, q, alpha (PF)
+  // Every LDS vector is padded to PDK floats, 4 after every 16 (column j at
+  // j + j / 16 * 4): the lanes of a row read 16-float runs, which would
+  // otherwise start 64 bytes apart and share LDS banks.
+  constexpr int PDK = DK + DK / 4;
+  float* pm = lds;                        // [LG][PARTS][PDK]
+  float* so = pm + LG * PARTS * PDK;      // [LG][PDK] scales before the step
+  float* sn = so + LG * PDK;              // [LG][PDK] new scales
+  float* si = sn + LG * PDK;              // [LG][PDK] new inverse scales
+  float* skq = si + LG * PDK;             // [3][PDK] the head's k, q, alpha (PF)
 
   const int tid = threadIdx.x;
   const int wv = tid / 64;
@@ -117,6 +121,7 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   const int lr = lane % LPR;
   const int rsub = lane / LPR;
   const int col0 = lr * E;
+  const int pcol0 = col0 + col0 / 4;  // the lane's run in the padded LDS vectors
   const LaneCodes<DK, BITS> lc(mask, lr);
   const float bias = lc.is8 ? 128.0f : 8.0f;
   uint8_t* hcodes = reinterpret_cast<uint8_t*>(p.state) + head_code_offset(p, sl.b, sl.h);
@@ -143,7 +148,8 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
 #pragma unroll
       for (int vi = 0; vi < NV; ++vi)
         for (int f = tid; f < DK / 4; f += 64 * NW)
-          reinterpret_cast<float4*>(skq + vi * DK)[f] = reinterpret_cast<const float4*>(src3[vi])[f];
+          reinterpret_cast<float4*>(skq + vi * PDK)[f + f / 4] =
+              reinterpret_cast<const float4*>(src3[vi])[f];
     } else {
       loadv(p.k + (size_t)sl.head * DK + col0, kk);
       loadv(p.q + (size_t)sl.head * DK + col0, qq);
@@ -187,7 +193,8 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     if constexpr (OP == kStep) {
       for (int t = tid; t < LG * DK; t += 64 * NW) {
         const int grow = base / G + t / DK;
-        so[t] = grow * G < p.dv ? hscales[(size_t)grow * DK + t % DK] : 0.0f;
+        const int j = t % DK;
+        so[(t / DK) * PDK + j + j / 16 * 4] = grow * G < p.dv ? hscales[(size_t)grow * DK + j] : 0.0f;
       }
     }
     // PF: the next block's codes and v (issued unconditionally, so that the
@@ -220,12 +227,12 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
         const int row = base + wv * RB + it * RPW + rsub;
         if constexpr (PF) {
           asm volatile("" ::: "memory");  // the head's vectors from LDS here, not held
-          lds_load(skq + col0, kk);
-          lds_load(skq + DK + col0, qq);
-          if constexpr (vector_decay(MIXER)) lds_load(skq + 2 * DK + col0, al);
+          lds_load(skq + pcol0, kk);
+          lds_load(skq + PDK + pcol0, qq);
+          if constexpr (vector_decay(MIXER)) lds_load(skq + 2 * PDK + pcol0, al);
         }
         float sc[E];
-        lds_load(so + lg * DK + col0, sc);
+        lds_load(so + lg * PDK + pcol0, sc);
         float d[E];
         if constexpr (BITS != 0)
           unpack16<BITS>(wc[it], d);
@@ -259,7 +266,7 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       for (int j = 0; j < E; ++j)
         cm[j] = first ? fabsf(sp[it][j]) : fmaxf(cm[j], fabsf(sp[it][j]));
       if (last) {
-        float* dst = pm + ((size_t)lg * PARTS + wv * RPW + rsub) * DK + col0;
+        float* dst = pm + ((size_t)lg * PARTS + wv * RPW + rsub) * PDK + pcol0;
 #pragma unroll
         for (int q4 = 0; q4 < E / 4; ++q4)
           reinterpret_cast<float4*>(dst)[q4] =
@@ -271,16 +278,17 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     // one thread per (row group, column): absmax, scale, inverse scale
     for (int t = tid; t < LG * DK; t += 64 * NW) {
       const int lg = t / DK, j = t % DK;
+      const int pj = j + j / 16 * 4;
       float m = 0.0f;
 #pragma unroll 8
-      for (int q = 0; q < PARTS; ++q) m = fmaxf(m, pm[((size_t)lg * PARTS + q) * DK + j]);
+      for (int q = 0; q < PARTS; ++q) m = fmaxf(m, pm[((size_t)lg * PARTS + q) * PDK + pj]);
       float s, inv;
       if constexpr (BITS != 0)
         group_scale<(1 << (BITS - 1)) - 1>(m, s, inv);
       else
         group_scale_rt(m, (mask >> (j / 16)) & 1u, s, inv);
-      sn[t] = s;
-      si[t] = inv;
+      sn[lg * PDK + pj] = s;
+      si[lg * PDK + pj] = inv;
       const int grow = base / G + lg;
       if (grow * G < p.dv) st_stream(hscales + (size_t)grow * DK + j, s);
     }
@@ -292,10 +300,10 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       const int lg = (wv * RB + it * RPW) / G;
       const int row = base + wv * RB + it * RPW + rsub;
       float inv16[E], s_old[E], s_new[E];
-      lds_load(si + lg * DK + col0, inv16);
+      lds_load(si + lg * PDK + pcol0, inv16);
       if constexpr (RND == kBDR) {
-        lds_load(so + lg * DK + col0, s_old);
-        lds_load(sn + lg * DK + col0, s_new);
+        lds_load(so + lg * PDK + pcol0, s_old);
+        lds_load(sn + lg * PDK + pcol0, s_new);
       }
       uint32_t out[4];
       const uint32_t block = (uint32_t)((row * DK + col0) >> 4);
@@ -396,7 +404,7 @@ __global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) __attribute__((amdgpu_waves
 void key_kernel(const KParams p) {
   using K = KGeo<DK, G>;
   constexpr bool PF = key_prefetch<OP, MIXER, RND, false>();
-  __shared__ float lds[K::LG * (K::PARTS + 3) * DK + (PF ? 3 * DK : 0)];
+  __shared__ float lds[(K::LG * (K::PARTS + 3) + (PF ? 3 : 0)) * (DK + DK / 4)];
   const Slice sl = wave_slice(p);
   if (p.int8_blocks[sl.h] != 0u)
     key_quant_head<OP, MIXER, RND, DK, 8, G, PF>(p, sl, lds);
@@ -410,7 +418,7 @@ template <int OP, int MIXER, int RND, int DK, int G>
 __global__ __launch_bounds__((64 * KGeo<DK, G>::NW)) void key_mixed_kernel(const KParams p) {
   using K = KGeo<DK, G>;
   constexpr bool PF = key_prefetch<OP, MIXER, RND, true>();
-  __shared__ float lds[K::LG * (K::PARTS + 3) * DK + (PF ? 3 * DK : 0)];
+  __shared__ float lds[(K::LG * (K::PARTS + 3) + (PF ? 3 : 0)) * (DK + DK / 4)];
   key_quant_head<OP, MIXER, RND, DK, 0, G, PF>(p, wave_slice(p), lds);
 }
 
