@@ -117,7 +117,7 @@ def test_config4_every_layer_every_head_reduced_batch():
 
 
 @pytest.mark.skipif(not EVERY, reason="set QSTATE_PARITY_EVERY_HEAD=1 (minutes of host time)")
-@pytest.mark.parametrize("wid,rounding", [(2, None), (3, W.RTN), (3, W.SR)])
+@pytest.mark.parametrize("wid,rounding", [(2, None), (2, W.BDR), (3, W.RTN), (3, W.SR)])
 def test_full_size_every_head_to_T(wid, rounding):
     w = W.WORKLOADS[wid]
     rep = _run(w, w.steps, rounding, tag="full-every")
