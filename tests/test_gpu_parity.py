@@ -171,6 +171,8 @@ WINDOW_RAGGED = [
     (W.KDA, W.RTN, 256, 45, 32, [4, 8], 4),
     (W.GLA, W.BDR, 128, 70, 64, [8, 4], 16),
     (W.SCALAR, W.SR, 256, 129, 128, [4], 8),
+    (W.KDA, W.BDR, 128, 70, 32, [4, 8], 8),
+    (W.GDN, W.BDR, 64, 40, 16, [4, 8, 4], 4),
 ]
 
 
