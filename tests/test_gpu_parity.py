@@ -70,6 +70,16 @@ def test_bdr_every_head(wid):
     _run(W.WORKLOADS[wid].scaled(B=2), 10, rounding=W.BDR)
 
 
+@pytest.mark.parametrize("mixer,G", [(W.GDN, 128), (W.GDN, 16), (W.SCALAR, 128)])
+def test_bdr_group_sizes(mixer, G):
+    """BDR with mostly INT4 heads at the group sizes the workloads do not use
+    (one group spanning four lanes, two groups per lane): persistent and
+    sliced steps alike."""
+    w = W.Workload(90 + G % 89, f"bdr_m{mixer}_g{G}", mixer, 2, 4, 128, 128, G, 6, 12, W.BDR,
+                   "int8")
+    _run(w, 12, hb=np.array([4, 4, 8, 4], np.uint8), seed=23)
+
+
 def test_bdr_full_size_sampled_heads():
     w = W.WORKLOADS[2]
     rng = np.random.default_rng(12)
