@@ -75,8 +75,8 @@ def test_bdr_group_sizes(mixer, G):
     """BDR with mostly INT4 heads at the group sizes the workloads do not use
     (one group spanning four lanes, two groups per lane): persistent and
     sliced steps alike."""
-    w = W.Workload(90 + G % 89, f"bdr_m{mixer}_g{G}", mixer, 2, 4, 128, 128, G, 6, 12, W.BDR,
-                   "int8")
+    w = W.Workload(90 + 10 * mixer + G // 16, f"bdr_m{mixer}_g{G}", mixer, 2, 4, 128, 128, G, 6,
+                   12, W.BDR, "int8")
     _run(w, 12, hb=np.array([4, 4, 8, 4], np.uint8), seed=23)
 
 
