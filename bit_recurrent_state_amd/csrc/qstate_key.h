@@ -185,12 +185,36 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
       v_[it] = vh[row];
     }
   };
+  // PFS: the old scales of a block's row groups are loaded with its codes,
+  // one block ahead, NSO per thread (in-bounds stand-ins past the slice,
+  // stored as zeros), so the block does not wait on them before its first
+  // barrier (KDA, at its register bound, keeps loading them per block).
+  constexpr bool PFS = PF && MIXER != kKDA;
+  constexpr int NSO = (LG * DK + 64 * NW - 1) / (64 * NW);
+  auto load_scales = [&](int base_, float (&sv)[NSO]) {
+#pragma unroll
+    for (int i = 0; i < NSO; ++i) {
+      const int t = tid + i * 64 * NW;
+      const int grow = base_ / G + t / DK, j = t % DK;
+      const bool ok = t < LG * DK && base_ < sl.r1 && grow * G < p.dv;
+      const float x = hscales[ok ? (size_t)grow * DK + j : (size_t)j];
+      sv[i] = ok ? x : 0.0f;
+    }
+  };
+  float son[NSO];
   uint32_t wc[NI][4] = {};
   float vr[NI] = {};
   if constexpr (PF) load_block(sl.r0, false, wc, vr);
+  if constexpr (PFS) load_scales(sl.r0, son);
   for (int base = sl.r0; base < sl.r1; base += BR) {
     // scales of the block's row groups before the step
-    if constexpr (OP == kStep) {
+    if constexpr (OP == kStep && PFS) {
+#pragma unroll
+      for (int i = 0; i < NSO; ++i) {
+        const int t = tid + i * 64 * NW, j = t % DK;
+        if (t < LG * DK) so[(t / DK) * PDK + j + j / 16 * 4] = son[i];
+      }
+    } else if constexpr (OP == kStep) {
       for (int t = tid; t < LG * DK; t += 64 * NW) {
         const int grow = base / G + t / DK;
         const int j = t % DK;
@@ -202,9 +226,10 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     // stand-in that is never used); otherwise this block's
     uint32_t wn[NI][4] = {};
     float vn[NI] = {};
-    if constexpr (PF)
+    if constexpr (PF) {
       load_block(base + BR, base + BR >= sl.r1, wn, vn);
-    else if constexpr (OP == kStep)
+      if constexpr (PFS) load_scales(base + BR, son);
+    } else if constexpr (OP == kStep)
       load_block(base, false, wc, vr);
     float sp[NI][E];
     if constexpr (OP == kImport) {
