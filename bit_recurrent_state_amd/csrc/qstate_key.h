@@ -207,6 +207,9 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   if constexpr (PF) load_block(sl.r0, false, wc, vr);
   if constexpr (PFS) load_scales(sl.r0, son);
   for (int base = sl.r0; base < sl.r1; base += BR) {
+    // without PF this block's codes and v, issued before its old scales so
+    // that the two loads' latencies overlap
+    if constexpr (OP == kStep && !PF) load_block(base, false, wc, vr);
     // scales of the block's row groups before the step
     if constexpr (OP == kStep && PFS) {
 #pragma unroll
@@ -223,14 +226,13 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     }
     // PF: the next block's codes and v (issued unconditionally, so that the
     // waits on this block's loads stay exact: after the last block a
-    // stand-in that is never used); otherwise this block's
+    // stand-in that is never used)
     uint32_t wn[NI][4] = {};
     float vn[NI] = {};
     if constexpr (PF) {
       load_block(base + BR, base + BR >= sl.r1, wn, vn);
       if constexpr (PFS) load_scales(base + BR, son);
-    } else if constexpr (OP == kStep)
-      load_block(base, false, wc, vr);
+    }
     float sp[NI][E];
     if constexpr (OP == kImport) {
 #pragma unroll
