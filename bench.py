@@ -89,6 +89,21 @@ def measured_traffic(w):
     return e["hbm_bytes_per_launch"]
 
 
+def measured_clock(w):
+    """Shader clock (GHz) of this workload's step kernel from the committed
+    rocprofv3 SQ_BUSY_CU_CYCLES record (median over dispatches); None when it
+    was not taken or the kernel source changed since."""
+    try:
+        import json as _j
+        t = _j.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(traffic_key(w))
+    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash(w):
+        return None
+    return e.get("shader_clock_ghz")
+
+
 def measured_valu(w):
     """VALU wave-instructions per launch from the committed rocprofv3
     SQ_INSTS_VALU count of this workload's step kernel; None when it was not
@@ -599,6 +614,10 @@ def main():
                                    "unit": "T lane-instructions/s", "frac": tl / VALU_PEAK_TLANES,
                                    "wave_insts_per_launch": vi,
                                    "lane_insts_per_state_element": vi * 64 / (w.B * w.H * w.dv * w.dk)}
+        clk = measured_clock(w)
+        if clk:  # the same issue rate at the clock the chip held during the step
+            result["valu_roofline"]["measured_clock_ghz"] = clk
+            result["valu_roofline"]["frac_at_measured_clock"] = tl / (VALU_PEAK_TLANES * clk / 2.4)
 
     if not args.no_extras:
         result["accuracy_vs_fp32_state"] = fp32_accuracy(w, hb, Q, torch)

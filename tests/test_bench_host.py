@@ -74,9 +74,11 @@ def test_profile_records_follow_the_kernel_source(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda w_: entry["kernel_source_sha256_16"])
     assert bench.measured_traffic(w) == entry["hbm_bytes_per_launch"]
     assert bench.measured_valu(w) == entry.get("valu_wave_insts_per_launch")
+    assert bench.measured_clock(w) == entry.get("shader_clock_ghz")
     monkeypatch.setattr(bench, "kernel_source_hash", lambda w_: "0" * 16)
     assert bench.measured_traffic(w) is None
     assert bench.measured_valu(w) is None
+    assert bench.measured_clock(w) is None
 
 
 def test_stored_records_are_calibrated():
