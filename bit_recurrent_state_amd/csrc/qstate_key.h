@@ -188,8 +188,11 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   // PFS: the old scales of a block's row groups are loaded with its codes,
   // one block ahead, NSO per thread (in-bounds stand-ins past the slice,
   // stored as zeros), so the block does not wait on them before its first
-  // barrier (KDA, at its register bound, keeps loading them per block).
+  // barrier.  KDA, at its register bound, issues them later instead, before
+  // the block's requantization (PFL, groups of 64 rows: with 32 or 128
+  // it spills), where fewer registers are live.
   constexpr bool PFS = PF && MIXER != kKDA;
+  constexpr bool PFL = PF && !PFS && G == 64;
   constexpr int NSO = (LG * DK + 64 * NW - 1) / (64 * NW);
   auto load_scales = [&](int base_, float (&sv)[NSO]) {
 #pragma unroll
@@ -205,13 +208,13 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
   uint32_t wc[NI][4] = {};
   float vr[NI] = {};
   if constexpr (PF) load_block(sl.r0, false, wc, vr);
-  if constexpr (PFS) load_scales(sl.r0, son);
+  if constexpr (PFS || PFL) load_scales(sl.r0, son);
   for (int base = sl.r0; base < sl.r1; base += BR) {
     // without PF this block's codes and v, issued before its old scales so
     // that the two loads' latencies overlap
     if constexpr (OP == kStep && !PF) load_block(base, false, wc, vr);
     // scales of the block's row groups before the step
-    if constexpr (OP == kStep && PFS) {
+    if constexpr (OP == kStep && (PFS || PFL)) {
 #pragma unroll
       for (int i = 0; i < NSO; ++i) {
         const int t = tid + i * 64 * NW, j = t % DK;
@@ -321,6 +324,7 @@ __device__ __forceinline__ void key_quant_head(const KParams& p, const Slice sl,
     }
     __syncthreads();  // new scales in LDS
 
+    if constexpr (PFL) load_scales(base + BR, son);
     // requantize and store
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
