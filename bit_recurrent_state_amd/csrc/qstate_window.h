@@ -167,7 +167,8 @@ template <int MIXER, int DK, int W, bool MERGE>
 __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl, const WinHead& wh,
                                                 int slot, bool writer, float beta, float alpha_s,
                                                 float* lds_bo, float* lds_c, float* lds_sa,
-                                                float& c_new, float& s_anew, float& inv_anew) {
+                                                float* lds_kq, float& c_new, float& s_anew,
+                                                float& inv_anew) {
   constexpr bool merge = MERGE;
   constexpr int LPP = DK / 16;         // lanes per pair
   constexpr int PPP = 64 / LPP;        // pairs per pass
@@ -179,6 +180,14 @@ __device__ __forceinline__ void window_prologue(const KParams& p, const Slice sl
   loadv(p.k + (size_t)sl.head * DK + c0, k16);
   loadv(p.q + (size_t)sl.head * DK + c0, q16);
   if constexpr (vector_decay(MIXER)) loadv(p.alpha + (size_t)sl.head * DK + c0, a16);
+  // the rows' copy of the head's vectors (padded, 4 floats after every 16),
+  // from the first pass's lanes, which together hold all dk columns
+  if (psub == 0) {
+    constexpr int PDK = DK + DK / 4;
+    storev(lds_kq + c0 + c0 / 4, k16);
+    storev(lds_kq + PDK + c0 + c0 / 4, q16);
+    if constexpr (vector_decay(MIXER)) storev(lds_kq + 2 * PDK + c0 + c0 / 4, a16);
+  }
   if (lane < W) lds_sa[lane] = wh.s_rd[2 * lane];
   c_new = row_sum<LPP>(chunk_dot(k16, q16, 0));
 #pragma unroll
@@ -305,21 +314,12 @@ __device__ __forceinline__ void step_pw_head(const KParams& p, const Slice sl, f
   float* lds_kq = lds_sa + W;  // the head's k, q and (GLA, KDA) alpha, [3][dk]
   constexpr bool merge = MERGE;
   float c_new, s_anew, inv_anew;
-  window_prologue<MIXER, DK, W, MERGE>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
-                                lds_sa, c_new, s_anew, inv_anew);
   // The rows read the head's vectors from LDS in every iteration instead of
   // holding them in registers (2 or 3 x E floats per lane), which keeps the
-  // kernel within the registers of four waves per SIMD.
-  {
-    constexpr int NV = vector_decay(MIXER) ? 3 : 2;
-    const float* src[3] = {p.k + (size_t)sl.head * DK, p.q + (size_t)sl.head * DK,
-                           vector_decay(MIXER) ? p.alpha + (size_t)sl.head * DK : nullptr};
-#pragma unroll
-    for (int vi = 0; vi < NV; ++vi)
-      for (int f = lane; f < DK / 4; f += 64)
-        reinterpret_cast<float4*>(lds_kq + vi * PDK)[f + f / 4] =
-            reinterpret_cast<const float4*>(src[vi])[f];
-  }
+  // kernel within the registers of four waves per SIMD; the prologue, which
+  // loads them for the keys' transition, leaves them there.
+  window_prologue<MIXER, DK, W, MERGE>(p, sl, wh, slot, sl.r0 == 0, beta, alpha_s, lds_bo, lds_c,
+                                lds_sa, lds_kq, c_new, s_anew, inv_anew);
   __syncthreads();
   float ca[W], sa[W];  // by age: 0 = oldest (leaving), W-1 = newest before this step
 #pragma unroll
